@@ -1,0 +1,208 @@
+"""CPU oracle for 4-bit group-wise weight quantization (NF4, INT4-sym, INT4-asym).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` import this package.  The product library
+never imports, links or calls it, and shares no code with it.
+
+The arithmetic lives in plain scalar C (``q4_oracle.c``, built with gcc, no
+fast-math) and is reached through ctypes; this module only marshals numpy
+arrays.  ``exact.py`` holds a tiny exact-rational re-derivation used to pin the
+C code on small inputs.
+
+What the oracle computes, and from which page (titles and sections of the web
+pages on 4-bit group-wise quantization):
+
+* "What is 4-bit quantization and why does it matter?", section "How 4-bit
+  quantization works": the affine formula, INT4-symmetric levels -8..7 with
+  scale max|w|/7, the printed NF4 table, the low-nibble-first unpack.
+* "INT4" (AI technologies atlas), "How it works" / "Components": asymmetric
+  levels 0..15 with an integer zero-point, FP16 per-group scales.
+* "Loading a model in 4-bit", "Block-wise quantisation, stated exactly":
+  contiguous blocks, absmax per block, nearest of 16 entries after dividing by
+  the absmax, dequantize = absmax times table value; "Where the accuracy goes":
+  the product is an ordinary 16-bit matmul on dequantized weights.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+NF4, INT4_SYM, INT4_ASYM = 0, 1, 2
+F16, BF16 = 0, 1
+FORMAT_NAMES = {NF4: "nf4", INT4_SYM: "int4_sym", INT4_ASYM: "int4_asym"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def build(force: bool = True) -> str:
+    """Compile q4_oracle.c into liboracle.so with gcc (IEEE, no contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-lm", "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    """Load the oracle library, building it first if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
+            L.orc_quantize.argtypes = [_int, _int, _u16p, _i64, _i64, _u8p, _vp, _u8p]
+            L.orc_dequantize.argtypes = [_int, _int, _u8p, _vp, _u8p, _i64, _i64, _int, _u16p]
+            L.orc_matmul.argtypes = [_int, _int, _int, _u16p, _i64, _u8p, _vp, _u8p,
+                                     _i64, _i64, _i64p, _i64, _f64p, _f64p]
+            for f in (L.orc_quantize, L.orc_dequantize, L.orc_matmul):
+                f.restype = _int
+            L.orc_nf4_nearest.argtypes = [ctypes.c_float]
+            L.orc_nf4_nearest.restype = _int
+            L.orc_f32_to_f16_array.argtypes = [_f32p, _u16p, _i64]
+            L.orc_f16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
+            L.orc_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
+            L.orc_nf4_nearest_array.argtypes = [_f32p, _u8p, _i64]
+            for f in (L.orc_f32_to_f16_array, L.orc_f16_to_f32_array,
+                      L.orc_f32_to_bf16_array, L.orc_nf4_nearest_array):
+                f.restype = None
+            _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def _check_g(g: int) -> None:
+    if g not in (32, 64, 128):
+        raise ValueError("group size must be 32, 64 or 128")
+
+
+def nf4_table() -> np.ndarray:
+    """The oracle's codebook, as float32[16]."""
+    arr = (ctypes.c_float * 16).in_dll(lib(), "orc_nf4_table")
+    return np.array(arr, dtype=np.float32)
+
+
+def f32_to_f16_bits(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().orc_f32_to_f16_array(_p(a, _f32p), _p(out, _u16p), a.size)
+    return out
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().orc_f16_to_f32_array(_p(h, _u16p), _p(out, _f32p), h.size)
+    return out
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16_array(_p(a, _f32p), _p(out, _u16p), a.size)
+    return out
+
+
+def nf4_nearest(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_nf4_nearest_array(_p(x, _f32p), _p(out, _u8p), x.size)
+    return out
+
+
+def quantize(fmt: int, g: int, w_bits: np.ndarray):
+    """Quantize fp16 weights given as uint16 bit patterns [N, K].
+
+    Returns (codes uint8[N, K/2], scales, zeros) where scales is float32[N, K/g]
+    for NF4 and uint16 fp16 bits [N, K/g] for INT4, and zeros is uint8
+    [ceil(N*K/g/2)] for INT4-asym, else None."""
+    _check_g(g)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    N, K = w.shape
+    if K % g:
+        raise ValueError("K must be a multiple of g")
+    G = K // g
+    codes = np.zeros((N, K // 2), dtype=np.uint8)
+    scales = np.zeros((N, G), dtype=np.float32 if fmt == NF4 else np.uint16)
+    zeros = np.zeros(((N * G + 1) // 2,), dtype=np.uint8) if fmt == INT4_ASYM else None
+    rc = lib().orc_quantize(fmt, g, _p(w, _u16p), N, K, _p(codes, _u8p),
+                            scales.ctypes.data_as(_vp),
+                            _p(zeros, _u8p) if zeros is not None else None)
+    if rc != 0:
+        raise ValueError("orc_quantize rejected its arguments")
+    return codes, scales, zeros
+
+
+def dequantize(fmt: int, g: int, codes, scales, zeros, N: int, K: int, out_t: int) -> np.ndarray:
+    """Dequantize to fp16 (F16) or bf16 (BF16) bit patterns, uint16[N, K]."""
+    _check_g(g)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales)
+    out = np.empty((N, K), dtype=np.uint16)
+    z = np.ascontiguousarray(zeros, dtype=np.uint8) if zeros is not None else None
+    rc = lib().orc_dequantize(fmt, g, _p(codes, _u8p), scales.ctypes.data_as(_vp),
+                              _p(z, _u8p) if z is not None else None, N, K, out_t,
+                              _p(out, _u16p))
+    if rc != 0:
+        raise ValueError("orc_dequantize rejected its arguments")
+    return out
+
+
+def matmul(fmt: int, g: int, act_t: int, x_bits, codes, scales, zeros, N: int, K: int,
+           rows=None):
+    """fp64 reference y = x . what^T on rows `rows` of W (all rows if None).
+
+    x_bits: uint16 [M, K] activation bit patterns in dtype act_t.
+    Returns (y float64 [M, nrows], absdot float64 [M, nrows]) where absdot is
+    sum_k |x * what|, the scale of the tolerance."""
+    _check_g(g)
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x.ndim == 1:
+        x = x[None, :]
+    M = x.shape[0]
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales)
+    z = np.ascontiguousarray(zeros, dtype=np.uint8) if zeros is not None else None
+    if rows is None:
+        r = None
+        nrows = N
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = r.size
+    y = np.empty((M, nrows), dtype=np.float64)
+    ad = np.empty((M, nrows), dtype=np.float64)
+    rc = lib().orc_matmul(fmt, g, act_t, _p(x, _u16p), M, _p(codes, _u8p),
+                          scales.ctypes.data_as(_vp), _p(z, _u8p) if z is not None else None,
+                          N, K, _p(r, _i64p) if r is not None else None, nrows,
+                          _p(y, _f64p), _p(ad, _f64p))
+    if rc != 0:
+        raise ValueError("orc_matmul rejected its arguments")
+    return y, ad
+
+
+def tolerance(absdot: np.ndarray) -> np.ndarray:
+    """Per-output bound for a GEMV/GEMM result: 2e-3 * sum|x*what| + 1e-3."""
+    return 2e-3 * absdot + 1e-3

@@ -1,0 +1,93 @@
+/*
+ * q4_oracle.h -- plain, slow CPU oracle for 4-bit group-wise weight quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product library
+ * (bit_group_wise_amd/libq4.so) never links, loads or calls it, and the two
+ * share no source: this file has its own codebook literal, its own fp16/bf16
+ * conversions and its own packing loops.
+ *
+ * Everything is scalar C, one element at a time, in the order the pages state
+ * the method.  Floating point follows IEEE binary32 / binary64 as written in C
+ * (compile with -O2 -ffp-contract=off, never -ffast-math).
+ *
+ * Sources (web pages on 4-bit group-wise quantization):
+ *   [n4n]   "What is 4-bit quantization and why does it matter?", section
+ *           "How 4-bit quantization works": affine quantize/dequantize formula,
+ *           INT4-symmetric levels -8..7 with scale max|w|/7, the printed
+ *           16-value NF4 table, the packed-uint8 unpack expression (low nibble
+ *           first) and the dequantize = table value times block scale step.
+ *   [atlas] "INT4" (AI technologies atlas), sections "How it works" and
+ *           "Components": asymmetric levels 0..15, integer zero-point, per-group
+ *           scale usually stored in FP16, groups of 32/64/128.
+ *   [hf4]   "Loading a model in 4-bit", section "Block-wise quantisation, stated
+ *           exactly": contiguous blocks, absmax c = max|w| per block, nearest of
+ *           the 16 codebook entries after dividing by c, dequantize c*Q[i].
+ *   [hf4]   section "Where the accuracy goes" and [bnb] "INT4 Quantization >
+ *           Practical Implementation with bitsandbytes": the matmul runs in the
+ *           16-bit compute dtype on dequantized weights.
+ */
+#ifndef Q4_ORACLE_H
+#define Q4_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Format and dtype ids (the same numbering as the product ABI, defined here
+ * independently). */
+enum { ORC_NF4 = 0, ORC_INT4_SYM = 1, ORC_INT4_ASYM = 2 };
+enum { ORC_F16 = 0, ORC_BF16 = 1 };
+
+/* The NF4 codebook as printed (16 binary32 values). */
+extern const float orc_nf4_table[16];
+
+/* IEEE conversions written from the format definitions: round to nearest,
+ * ties to even; fp16 subnormals are produced and consumed (no flush);
+ * overflow gives infinity. */
+float    orc_f16_to_f32(uint16_t h);
+uint16_t orc_f32_to_f16(float f);
+float    orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16(float f);
+
+/* Element-wise array forms of the conversions (n values). */
+void orc_f32_to_f16_array(const float *in, uint16_t *out, int64_t n);
+void orc_f16_to_f32_array(const uint16_t *in, float *out, int64_t n);
+void orc_f32_to_bf16_array(const float *in, uint16_t *out, int64_t n);
+
+/* Nearest NF4 index of a binary32 value x (ties to the lower index). */
+int orc_nf4_nearest(float x);
+void orc_nf4_nearest_array(const float *in, uint8_t *out, int64_t n);
+
+/* Quantize a row-major fp16 weight W[N][K] (bit patterns) with groups of g
+ * contiguous elements along K.
+ *   codes  : uint8[N*K/2], byte t = nib[2t] | nib[2t+1] << 4 (flat order)
+ *   scales : NF4 -> float[N*K/g] (absmax), INT4 -> uint16 fp16 bits [N*K/g]
+ *   zeros  : INT4-asym only, uint8[ceil(N*K/g / 2)], zero-points packed two
+ *            per byte in flat group order, low nibble first; NULL otherwise.
+ * Returns 0, or -1 on a bad argument (K % g != 0, unknown format, ...). */
+int orc_quantize(int fmt, int g, const uint16_t *w, int64_t N, int64_t K,
+                 uint8_t *codes, void *scales, uint8_t *zeros);
+
+/* Dequantize to fp16 (out_t = ORC_F16) or bf16 (ORC_BF16) bit patterns,
+ * out[N*K]. Returns 0 or -1. */
+int orc_dequantize(int fmt, int g, const uint8_t *codes, const void *scales,
+                   const uint8_t *zeros, int64_t N, int64_t K, int out_t,
+                   uint16_t *out);
+
+/* Reference product y[m][j] = sum_k x[m][k] * what[rows[j]][k] in binary64,
+ * summed in k order, where what is the dequantized weight rounded to the
+ * activation dtype act_t (x is given as act_t bit patterns, [M][K]).
+ * absdot[m][j] = sum_k |x[m][k] * what[rows[j]][k]| (the tolerance scale).
+ * rows == NULL means rows 0..N-1 (nrows must then equal N).
+ * Returns 0 or -1. */
+int orc_matmul(int fmt, int g, int act_t, const uint16_t *x, int64_t M,
+               const uint8_t *codes, const void *scales, const uint8_t *zeros,
+               int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+               double *y, double *absdot);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
