@@ -1,0 +1,165 @@
+// q4_api.hip -- the C ABI of libq4 (declared in include/q4.h): host-side
+// argument validation, status mapping and dispatch to the kernel launchers.
+// Every check runs before the first HIP call, so a bad argument never reaches
+// the runtime and the checks can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "q4.h"
+#include "q4_internal.hpp"
+
+namespace {
+
+bool format_ok(q4_format f) { return f == Q4_NF4 || f == Q4_INT4_SYM || f == Q4_INT4_ASYM; }
+bool dtype_ok(q4_dtype t) { return t == Q4_F16 || t == Q4_BF16; }
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Checks shared by every entry point that takes a quantized weight.
+q4_status check_weight(q4_format f, int g, const void *codes, const void *scales,
+                       const void *zeros, int64_t N, int64_t K)
+{
+    if (!format_ok(f) || !group_ok(g))
+        return Q4_EUNSUPPORTED;
+    if (!codes || !scales)
+        return Q4_EINVAL;
+    if (N <= 0 || K <= 0 || K % g != 0)
+        return Q4_EINVAL;
+    if ((f == Q4_INT4_ASYM) != (zeros != nullptr))
+        return Q4_EINVAL;
+    if (!aligned(codes, 16) || !aligned(scales, f == Q4_NF4 ? 4 : 2))
+        return Q4_EALIGN;
+    return Q4_OK;
+}
+
+q4_status from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_codes_bytes(int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0 || K % 2 != 0)
+        return 0;
+    return (size_t)(N * K / 2);
+}
+
+size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g)
+{
+    if (!format_ok(f) || !group_ok(g) || N <= 0 || K <= 0 || K % g != 0)
+        return 0;
+    return (size_t)(N * (K / g)) * (f == Q4_NF4 ? 4u : 2u);
+}
+
+size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g)
+{
+    if (!format_ok(f) || !group_ok(g) || N <= 0 || K <= 0 || K % g != 0)
+        return 0;
+    if (f != Q4_INT4_ASYM)
+        return 0;
+    return (size_t)((N * (K / g) + 1) / 2);
+}
+
+const char *q4_status_str(q4_status s)
+{
+    switch (s) {
+    case Q4_OK:
+        return "ok";
+    case Q4_EINVAL:
+        return "invalid argument";
+    case Q4_EUNSUPPORTED:
+        return "unsupported format, dtype, group size or shape";
+    case Q4_EALIGN:
+        return "misaligned pointer";
+    case Q4_EHIP:
+        return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+q4_status q4_quantize(q4_format f, int g, const void *w_f16, int64_t N, int64_t K,
+                      uint8_t *codes, void *scales, uint8_t *zeros, void *stream)
+{
+    q4_status st = check_weight(f, g, codes, scales, zeros, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!w_f16)
+        return Q4_EINVAL;
+    if (!aligned(w_f16, 16))
+        return Q4_EALIGN;
+    return from_hip(q4::launch_quantize(f, g, w_f16, N, K, codes, scales, zeros,
+                                        (hipStream_t)stream));
+}
+
+q4_status q4_dequantize(q4_format f, int g, const uint8_t *codes, const void *scales,
+                        const uint8_t *zeros, int64_t N, int64_t K, q4_dtype out_t,
+                        void *out, void *stream)
+{
+    q4_status st = check_weight(f, g, codes, scales, zeros, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!dtype_ok(out_t))
+        return Q4_EUNSUPPORTED;
+    if (!out)
+        return Q4_EINVAL;
+    if (!aligned(out, 16))
+        return Q4_EALIGN;
+    return from_hip(q4::launch_dequantize(f, g, codes, scales, zeros, N, K, out_t, out,
+                                          (hipStream_t)stream));
+}
+
+static q4_status check_product(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                               const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                               int64_t N, int64_t K, void *y)
+{
+    q4_status st = check_weight(f, g, codes, scales, zeros, N, K);
+    if (st != Q4_OK)
+        return st;
+    if (!dtype_ok(act_t))
+        return Q4_EUNSUPPORTED;
+    if (!x || !y || M <= 0)
+        return Q4_EINVAL;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return Q4_EUNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(y, 2))
+        return Q4_EALIGN;
+    return Q4_OK;
+}
+
+q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, void *y, void *stream)
+{
+    q4_status st = check_product(f, g, act_t, x, M, codes, scales, zeros, N, K, y);
+    if (st != Q4_OK)
+        return st;
+    if (M > 16)
+        return Q4_EUNSUPPORTED;
+    return from_hip(q4::launch_gemv(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
+                                    (hipStream_t)stream));
+}
+
+q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, void *y, void *stream)
+{
+    q4_status st = check_product(f, g, act_t, x, M, codes, scales, zeros, N, K, y);
+    if (st != Q4_OK)
+        return st;
+    return from_hip(q4::launch_gemm(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+int q4::device_cu_count()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}

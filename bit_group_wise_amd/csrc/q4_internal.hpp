@@ -1,0 +1,28 @@
+// q4_internal.hpp -- launchers shared between the C-ABI front end
+// (q4_api.hip) and the kernel files.  Arguments arrive validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "q4.h"
+
+namespace q4 {
+
+// Number of compute units of the current device (queried per call).
+int device_cu_count();
+
+hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t K,
+                           uint8_t *codes, void *scales, uint8_t *zeros, hipStream_t s);
+hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const void *scales,
+                             const uint8_t *zeros, int64_t N, int64_t K, q4_dtype out_t,
+                             void *out, hipStream_t s);
+hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                       const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                       int64_t N, int64_t K, void *y, hipStream_t s);
+hipError_t launch_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                       const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                       int64_t N, int64_t K, void *y, hipStream_t s);
+
+}  // namespace q4

@@ -1,0 +1,233 @@
+// quantize.hip -- fp16 weights -> packed 4-bit codes + per-group metadata.
+//
+// Method ("Loading a model in 4-bit", "Block-wise quantisation, stated
+// exactly"; "What is 4-bit quantization and why does it matter?", "How 4-bit
+// quantization works"; "INT4", "How it works" / "Components"): per group of g
+// contiguous weights, reduce the absmax (NF4, INT4-sym) or the zero-anchored
+// range (INT4-asym), form the stored scale, code each weight to the nearest
+// level after an IEEE binary32 division by the stored scale, and pack two
+// codes per byte, low nibble first.
+//
+// gfx950 mapping: the weight matrix is streamed as a flat array.  Each lane
+// owns 8 consecutive fp16 (one 16-byte load) and writes their 8 nibbles as
+// one dword, so a wave reads 1 KB and writes 256 B per step, fully
+// coalesced.  A group spans g/8 adjacent lanes and is reduced with
+// cross-lane shuffles.  The quotient w / s is formed from one correctly
+// rounded reciprocal per group plus Markstein's correction (q0 = w*r;
+// e = fma(-q0, s, w); q = fma(e, r, q0)), which equals the correctly rounded
+// IEEE quotient for every pair of fp16 operands with s > 0 (checked
+// exhaustively on all such pairs); NF4 codes come from a 33-bucket table of
+// exact decision thresholds held in LDS.
+#include "q4_common.hpp"
+#include "q4_internal.hpp"
+
+namespace q4 {
+namespace {
+
+constexpr int kBlock = 256;  // 4 waves
+constexpr int kUnroll = 4;   // 16-byte loads in flight per lane
+
+__constant__ NF4Bucket c_buckets[33] = {
+#define B(i) {kNF4Buckets.e[i].thr, kNF4Buckets.e[i].base}
+    B(0),  B(1),  B(2),  B(3),  B(4),  B(5),  B(6),  B(7),  B(8),  B(9),  B(10),
+    B(11), B(12), B(13), B(14), B(15), B(16), B(17), B(18), B(19), B(20), B(21),
+    B(22), B(23), B(24), B(25), B(26), B(27), B(28), B(29), B(30), B(31), B(32),
+#undef B
+};
+
+// Correctly rounded a / b given r = RN(1 / b) (Markstein).
+__device__ __forceinline__ float div_mk(float a, float b, float r)
+{
+    float q0 = a * r;
+    float e = __builtin_fmaf(-q0, b, a);
+    return __builtin_fmaf(e, r, q0);
+}
+
+template <int LPG>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int d = 1; d < LPG; d <<= 1)
+        v = fmaxf(v, __shfl_xor(v, d));
+    return v;
+}
+template <int LPG>
+__device__ __forceinline__ float group_min(float v)
+{
+#pragma unroll
+    for (int d = 1; d < LPG; d <<= 1)
+        v = fminf(v, __shfl_xor(v, d));
+    return v;
+}
+
+template <int FMT, int G>
+__global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restrict__ w,
+                                                          uint32_t *__restrict__ codes,
+                                                          void *__restrict__ scales,
+                                                          uint8_t *__restrict__ zeros,
+                                                          int64_t n_slots, int64_t n_groups)
+{
+    constexpr int LPG = G / 8;  // lanes per group
+    __shared__ NF4Bucket lut[33];
+    if constexpr (FMT == Q4_NF4) {
+        if (threadIdx.x < 33)
+            lut[threadIdx.x] = c_buckets[threadIdx.x];
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & 63;
+    const int64_t waves_per_block = kBlock / 64;
+    const int64_t wave = (int64_t)blockIdx.x * waves_per_block + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)gridDim.x * waves_per_block;
+
+    for (int64_t t0 = wave * kUnroll; t0 * 64 < n_slots; t0 += n_waves * kUnroll) {
+        u32x4 raw[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            int64_t slot = (t0 + u) * 64 + lane;
+            raw[u] = slot < n_slots ? w[slot] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t slot = (t0 + u) * 64 + lane;
+            const bool in = slot < n_slots;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = h2f(raw[u][i] & 0xffffu);
+                v[2 * i + 1] = h2f(raw[u][i] >> 16);
+            }
+            uint32_t word = 0;
+            const int64_t gi = slot / LPG;
+            const bool leader = (lane % LPG) == 0;
+            if constexpr (FMT == Q4_NF4) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    a = fmaxf(a, fabsf(v[i]));
+                const float c = group_max<LPG>(a);
+                if (c != 0.0f) {
+                    const float r = 1.0f / c;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float x = div_mk(v[i], c, r);
+                        // |x| <= 1, so b <= 32; the min only guards inputs
+                        // that break the finite-input precondition
+                        const uint32_t b = min((uint32_t)((x + 1.0f) * 16.0f), 32u);
+                        const NF4Bucket e = lut[b];
+                        const uint32_t code = e.base + (x >= e.thr ? 1u : 0u);
+                        word |= code << (4 * i);
+                    }
+                } else {
+                    word = 0x77777777u;
+                }
+                if (in && leader)
+                    ((float *)scales)[gi] = c;
+            } else if constexpr (FMT == Q4_INT4_SYM) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    a = fmaxf(a, fabsf(v[i]));
+                a = group_max<LPG>(a);
+                const uint32_t s16 = f2h_bits(a / 7.0f);
+                const float s = h2f(s16);
+                if (s != 0.0f) {
+                    const float r = 1.0f / s;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int q = (int)__builtin_rintf(div_mk(v[i], s, r));
+                        q = q < -8 ? -8 : (q > 7 ? 7 : q);
+                        word |= (uint32_t)(q + 8) << (4 * i);
+                    }
+                } else {
+                    word = 0x88888888u;
+                }
+                if (in && leader)
+                    ((uint16_t *)scales)[gi] = (uint16_t)s16;
+            } else {
+                float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    lo = fminf(lo, v[i]);
+                    hi = fmaxf(hi, v[i]);
+                }
+                lo = group_min<LPG>(lo);
+                hi = group_max<LPG>(hi);
+                const uint32_t s16 = f2h_bits((hi - lo) / 15.0f);
+                const float s = h2f(s16);
+                int z = 0;
+                if (s != 0.0f) {
+                    const float r = 1.0f / s;
+                    z = (int)__builtin_rintf(div_mk(-lo, s, r));
+                    z = z < 0 ? 0 : (z > 15 ? 15 : z);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int q = (int)__builtin_rintf(div_mk(v[i], s, r)) + z;
+                        q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                        word |= (uint32_t)q << (4 * i);
+                    }
+                }
+                // zero-points: the leader of an even group packs its own and
+                // the next group's (LPG lanes further on; both groups lie in
+                // the same 64-lane step because 512 / g is even)
+                const int z_next = __shfl_down(z, LPG);
+                if (in && leader) {
+                    ((uint16_t *)scales)[gi] = (uint16_t)s16;
+                    if ((gi & 1) == 0) {
+                        const uint32_t hi_nib = (gi + 1 < n_groups) ? (uint32_t)z_next : 0u;
+                        zeros[gi >> 1] = (uint8_t)((uint32_t)z | (hi_nib << 4));
+                    }
+                }
+            }
+            if (in)
+                codes[slot] = word;
+        }
+    }
+}
+
+template <int FMT>
+hipError_t launch_fmt(int g, const void *w, int64_t N, int64_t K, uint8_t *codes, void *scales,
+                      uint8_t *zeros, hipStream_t s)
+{
+    const int64_t n_slots = N * K / 8;
+    const int64_t n_groups = N * K / g;
+    const int64_t per_block = (int64_t)kBlock * kUnroll;  // slots per block step
+    int64_t blocks = (n_slots + per_block - 1) / per_block;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    if (blocks > cap)
+        blocks = cap;
+    dim3 grid((unsigned)blocks), block(kBlock);
+    const u32x4 *wp = (const u32x4 *)w;
+    uint32_t *cp = (uint32_t *)codes;
+    switch (g) {
+    case 32:
+        hipLaunchKernelGGL((quantize_kernel<FMT, 32>), grid, block, 0, s, wp, cp, scales, zeros,
+                           n_slots, n_groups);
+        break;
+    case 64:
+        hipLaunchKernelGGL((quantize_kernel<FMT, 64>), grid, block, 0, s, wp, cp, scales, zeros,
+                           n_slots, n_groups);
+        break;
+    default:
+        hipLaunchKernelGGL((quantize_kernel<FMT, 128>), grid, block, 0, s, wp, cp, scales, zeros,
+                           n_slots, n_groups);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t K,
+                           uint8_t *codes, void *scales, uint8_t *zeros, hipStream_t s)
+{
+    switch (f) {
+    case Q4_NF4:
+        return launch_fmt<Q4_NF4>(g, w, N, K, codes, scales, zeros, s);
+    case Q4_INT4_SYM:
+        return launch_fmt<Q4_INT4_SYM>(g, w, N, K, codes, scales, zeros, s);
+    default:
+        return launch_fmt<Q4_INT4_ASYM>(g, w, N, K, codes, scales, zeros, s);
+    }
+}
+
+}  // namespace q4

@@ -1,0 +1,133 @@
+/*
+ * q4.h -- C ABI of libq4: 4-bit group-wise LLM weight quantization on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Four operations: quantize fp16 weights to packed 4-bit codes plus per-group
+ * metadata, dequantize them back to fp16/bf16, and multiply activations by
+ * the quantized weights without materialising them (y = x . W^T), as a decode
+ * GEMV (1 <= M <= 16) and a prefill GEMM (any M).
+ *
+ * Definitions this library implements (web pages on 4-bit group-wise
+ * quantization, cited by title and section):
+ *   - "What is 4-bit quantization and why does it matter?", "How 4-bit
+ *     quantization works": quantized = round((w - zero_point) / scale),
+ *     dequantized = quantized * scale + zero_point; INT4-symmetric levels
+ *     -8..7 with an implicit zero and scale = max|w| / 7; NF4's 16 values
+ *     (the printed table, used verbatim); weights stored as packed uint8 with
+ *     the low nibble holding the earlier element; dequantize = table value
+ *     times the block scale.
+ *   - "INT4" (AI technologies atlas), "How it works" and "Components":
+ *     asymmetric levels 0..15 with an integer zero-point; per-group scale
+ *     usually stored in FP16; groups of 32, 64 or 128 weights.
+ *   - "Loading a model in 4-bit", "Block-wise quantisation, stated exactly":
+ *     contiguous blocks, absmax c = max|w| stored per block, each weight coded
+ *     as the nearest of the 16 codebook entries after dividing by c,
+ *     dequantized as c * Q[i]; "Where the accuracy goes": the layer
+ *     dequantizes to the 16-bit compute dtype and runs an ordinary 16-bit
+ *     matmul (fp32 accumulation here).
+ *
+ * Data layout (all row-major, W is [N, K] like a Linear layer's weight):
+ *   w       fp16 [N, K]
+ *   codes   uint8 [N, K/2]; byte t of the flat array holds element 2t in its
+ *           low nibble and element 2t+1 in its high nibble.
+ *   scales  NF4: float32 [N, K/g] (the block absmax c)
+ *           INT4-sym / INT4-asym: fp16 [N, K/g]
+ *   zeros   INT4-asym only: uint8 [ceil(N*K/g / 2)], the integer zero-points
+ *           (0..15) of the groups in flat order r*(K/g) + j, two per byte,
+ *           low nibble first.  NULL for the other formats.
+ *   x       [M, K] fp16 or bf16 (act_t); y [M, N] in the same dtype.
+ * A group is g contiguous elements of one row (K % g == 0).
+ *
+ * Coding rules (bit-exact, no fast-math; binary32 IEEE division by the
+ * stored scale, round-half-even):
+ *   NF4   c = max|w|; code = index of the nearest table entry to w / c, ties
+ *         to the lower index; c == 0 gives code 7 (the entry 0.0).
+ *   SYM   s = fp16(max|w| / 7); nibble = clamp(rint(w / s), -8, 7) + 8;
+ *         s == 0 gives nibble 8.
+ *   ASYM  lo = min(0, min w), hi = max(0, max w); s = fp16((hi - lo) / 15);
+ *         z = clamp(rint(-lo / s), 0, 15); nibble = clamp(rint(w / s) + z,
+ *         0, 15); s == 0 gives z = 0 and nibble 0.
+ * Dequantize: NF4 Q[i] * c, SYM (nibble - 8) * s, ASYM (nibble - z) * s, one
+ * binary32 product rounded once (nearest-even) to fp16 or bf16.
+ *
+ * Conventions:
+ *   - Ownership: every buffer is device memory owned by the caller.  The
+ *     library never allocates, frees or retains memory, keeps no state
+ *     between calls and never synchronises; it only enqueues kernels on
+ *     `stream` (a hipStream_t; NULL selects the null stream).  Its only
+ *     globals are read-only constant tables, so calls are thread-safe.
+ *   - Errors: every call validates its arguments on the host, before any HIP
+ *     call, and returns a q4_status.  Nothing aborts and no C++ exception
+ *     crosses the ABI.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Alignment: w, codes, x and out must be 16-byte aligned (the kernels
+ *     move 16 bytes per lane); scales must be 4-byte (NF4) or 2-byte (INT4)
+ *     aligned, y 2-byte aligned.  There is no slow fallback path.
+ *   - Preconditions not checked: inputs are finite; output buffers do not
+ *     alias inputs; the buffers are at least the sizes q4_*_bytes report.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { Q4_NF4 = 0, Q4_INT4_SYM = 1, Q4_INT4_ASYM = 2 } q4_format;
+typedef enum { Q4_F16 = 0, Q4_BF16 = 1 } q4_dtype;
+typedef enum {
+    Q4_OK = 0,
+    Q4_EINVAL = 1,       /* null pointer, N/K/M <= 0, K % g != 0, zeros given
+                            (or missing) for the format */
+    Q4_EUNSUPPORTED = 2, /* unknown format or dtype, g not in {32, 64, 128},
+                            M > 16 for q4_gemv */
+    Q4_EALIGN = 3,       /* a pointer violates the alignment rules above */
+    Q4_EHIP = 4          /* the HIP runtime refused a launch */
+} q4_status;
+
+/* Sizes in bytes of the caller-allocated buffers for an [N, K] weight with
+ * groups of g (0 for invalid arguments). */
+size_t q4_codes_bytes(int64_t N, int64_t K);                      /* N*K/2 */
+size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4) */
+size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g);  /* asym: ceil(N*K/g / 2), else 0 */
+
+/* Quantize fp16 weights w[N, K] into codes, scales and (asym) zeros.
+ * Sources: the coding rules above ("How 4-bit quantization works";
+ * "How it works" / "Components"; "Block-wise quantisation, stated exactly"). */
+q4_status q4_quantize(q4_format f, int g, const void *w_f16, int64_t N, int64_t K,
+                      uint8_t *codes, void *scales, uint8_t *zeros, void *stream);
+
+/* Dequantize into out[N, K] of dtype out_t (fp16 or bf16).
+ * Source: the dequantize rule above ("How 4-bit quantization works":
+ * table value times the block scale; the affine inverse). */
+q4_status q4_dequantize(q4_format f, int g, const uint8_t *codes, const void *scales,
+                        const uint8_t *zeros, int64_t N, int64_t K, q4_dtype out_t,
+                        void *out, void *stream);
+
+/* Decode-shape product y[M, N] = x[M, K] . What^T for 1 <= M <= 16, reading
+ * the packed weights once and dequantizing them in registers; fp32
+ * accumulation, one rounding of y to act_t.  Equal to a 16-bit matmul on the
+ * dequantized weights up to rounding order ("Where the accuracy goes").
+ * M > 16 returns Q4_EUNSUPPORTED (use q4_gemm). */
+q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, void *y, void *stream);
+
+/* Prefill-shape product y[M, N] = x[M, K] . What^T for any M >= 1: weight
+ * tiles are dequantized to the activation dtype in LDS and multiplied on the
+ * matrix cores with fp32 accumulation; y is rounded once to act_t. */
+q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, void *y, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *q4_status_str(q4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */
