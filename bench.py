@@ -1,0 +1,357 @@
+"""Benchmark of the 4-bit group-wise hot path on one MI355X.
+
+Default workload: a 7B-style decoder weight stream in NF4 (block 64, fp32
+absmax): 32 layers of q/k/v/o (4096x4096), gate/up (11008x4096) and down
+(4096x11008), all ~ N(0, 0.02^2) fp16, seeded.  q/k/v and gate/up, which share
+their input, are stored as row-concatenated matrices (codes are row-local, so
+the bytes are those of the separate matrices), giving 4 GEMV launches per
+layer and 128 per token.
+
+One step = one decode token: the 128 dequant-GEMVs (M = 1, bf16 activations)
+over all 6,476,005,376 weights, replayed from a captured HIP graph.  `value`
+is the weight bytes (codes + absmax) streamed per token times tokens/s.
+
+The same run also measures, each with HIP events on the launch stream:
+  * the one-shot quantize of all weights (HBM-resident fp16 input),
+  * dequantize of a 14336x4096 INT4-asym weight to bf16,
+  * the prefill GEMM M=2048, N=14336, K=4096, INT4-asym g32, bf16 x
+    (TFLOP/s against the dense bf16 matrix-core peak),
+  * the CPU oracle on a time-bounded sample of the token (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, TFLOP/s
+
+LAYERS = 32
+HID, FFN = 4096, 11008
+# fused launch matrices of one layer: (name, N, K, [(part, rows, seed index)])
+LAYER_MATS = [
+    ("qkv", 3 * HID, HID, [("q", HID, 0), ("k", HID, 1), ("v", HID, 2)]),
+    ("o", HID, HID, [("o", HID, 3)]),
+    ("gate_up", 2 * FFN, HID, [("gate", FFN, 4), ("up", FFN, 5)]),
+    ("down", HID, FFN, [("down", HID, 6)]),
+]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--layers", type=int, default=LAYERS,
+                   help="decoder layers in the weight stream (32 for the 7B shape)")
+    p.add_argument("--no-graph", action="store_true", help="time plain stream launches only")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="time budget of the CPU-oracle sample")
+    p.add_argument("--skip-extra", action="store_true",
+                   help="time only the decode token (for profiler runs)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                          "--gpus N > 1 is not supported"}))
+        sys.exit(2)
+
+    import torch
+    from bit_group_wise_amd import q4
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------- weights
+    t0 = time.time()
+    gen = torch.Generator(device=dev)
+    fp16 = []       # per layer: list of fused fp16 matrices
+    for layer in range(args.layers):
+        mats = []
+        for name, N, K, parts in LAYER_MATS:
+            w = torch.empty((N, K), dtype=torch.float16, device=dev)
+            r0 = 0
+            for _, rows, idx in parts:
+                gen.manual_seed(5000 + 7 * layer + idx)
+                w[r0:r0 + rows].normal_(0.0, 0.02, generator=gen)
+                r0 += rows
+            mats.append(w)
+        fp16.append(mats)
+    torch.cuda.synchronize()
+    log(f"generated fp16 weights in {time.time() - t0:.1f}s")
+
+    qw = [[q4.alloc_quantized(q4.NF4, 64, w.shape[0], w.shape[1], dev) for w in mats]
+          for mats in fp16]
+    n_weights = sum(w.numel() for mats in fp16 for w in mats)
+    w_bytes = sum(q.nbytes() for row in qw for q in row)
+
+    # ---------------------------------------------------------- one-shot quantize
+    def quantize_all():
+        for mats, qs in zip(fp16, qw):
+            for w, q in zip(mats, qs):
+                q4.quantize(w, q4.NF4, 64, out=q)
+
+    quantize_all()                              # warm (and the weights used below)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    quantize_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1)
+    quant_bytes = n_weights * 2 + w_bytes
+    del fp16
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------- decode token
+    xg = torch.Generator(device="cpu")
+    xg.manual_seed(5900)
+    x_h = torch.randn((1, HID), generator=xg).to(torch.bfloat16).to(dev)
+    xg.manual_seed(5901)
+    x_f = torch.randn((1, FFN), generator=xg).to(torch.bfloat16).to(dev)
+    outs = [[torch.empty((1, q.N), dtype=torch.bfloat16, device=dev) for q in row] for row in qw]
+
+    def token():
+        for qs, ys in zip(qw, outs):
+            for (name, N, K, _), q, y in zip(LAYER_MATS, qs, ys):
+                q4.gemv(x_f if K == FFN else x_h, q, out=y)
+
+    token()
+    torch.cuda.synchronize()
+    eager_ref = [y.clone() for ys in outs for y in ys]
+
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            token()                                # warm on the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            token()
+        torch.cuda.synchronize()
+        for rep in range(3):                       # replays must match eager
+            for ys in outs:
+                for y in ys:
+                    y.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            flat = [y for ys in outs for y in ys]
+            if not all(torch.equal(a, b) for a, b in zip(flat, eager_ref)):
+                log("graph replay differs from eager launches: timing eager launches")
+                graph = None
+                break
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            token()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_wall = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms = e0.elapsed_time(e1) / args.steps
+    value = w_bytes / (ms * 1e-3) / 1e9
+
+    # eager (no graph) rate for context
+    for _ in range(2):
+        token()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(max(args.steps // 5, 3)):
+        token()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / max(args.steps // 5, 3)
+
+    # per-launch GEMV durations (events around each launch on its stream)
+    ev = []
+    for qs, ys in zip(qw, outs):
+        for (name, N, K, _), q, y in zip(LAYER_MATS, qs, ys):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            q4.gemv(x_f if K == FFN else x_h, q, out=y)
+            b.record(stream)
+            ev.append((name, q.nbytes(), a, b))
+    torch.cuda.synchronize()
+    per = {}
+    tot_b = tot_ms = 0.0
+    for name, nb, a, b in ev:
+        d = a.elapsed_time(b)
+        per.setdefault(name, []).append((nb, d))
+        tot_b += nb
+        tot_ms += d
+    gemv_avg_us = tot_ms / len(ev) * 1e3
+    gemv_gbs = tot_b / (tot_ms * 1e-3) / 1e9
+    per_kernel = {n: {"bytes": v[0][0], "avg_us": round(sum(d for _, d in v) / len(v) * 1e3, 2),
+                      "GBps": round(v[0][0] / (sum(d for _, d in v) / len(v) * 1e-3) / 1e9, 1)}
+                  for n, v in per.items()}
+
+    extra = {}
+    if not args.skip_extra:
+        extra = extra_legs(torch, q4, dev, stream)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    result = {
+        "metric": "W4A16 dequant-GEMV weight GB/s (% HBM peak); GEMM TFLOP/s at M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "7B-style decode token: 32 layers x (qkv 12288x4096, o 4096x4096, "
+                        "gate_up 22016x4096, down 4096x11008), NF4 block 64 fp32 absmax, "
+                        "M=1 bf16 x, 128 dequant-GEMVs per step"
+                        + ("" if args.layers == LAYERS else f" ({args.layers} layers)"),
+            "weights": n_weights,
+            "weight_bytes_per_token": w_bytes,
+            "launch": "hip graph replay" if graph is not None else "stream launches",
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+            "eager_ms_per_step": round(eager_ms, 4),
+            "eager_GBps": round(w_bytes / (eager_ms * 1e-3) / 1e9, 1),
+            "wall_ms_per_step": round(wall_ms / args.steps, 4),
+            "gemv_per_matrix": per_kernel,
+            "quantize_all_ms": round(quant_ms, 3),
+            "quantize_all_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+            "device": props.name,
+            "cus": props.multi_processor_count,
+            **extra,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel<NF4, bf16, M=1>",
+            "achieved": round(gemv_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(gemv_avg_us, 3),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def extra_legs(torch, q4, dev, stream):
+    """Dequantize and prefill-GEMM legs on the INT4-asym g32 14336x4096 weight."""
+    N, K, M = 14336, 4096, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(401)
+    w = torch.empty((N, K), dtype=torch.float16, device=dev).normal_(0.001, 0.02, generator=gen)
+    gen.manual_seed(402)
+    x = torch.empty((M, K), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
+    x = x.to(torch.bfloat16)
+    q = q4.quantize(w, q4.INT4_ASYM, 32)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    qt = timed(lambda: q4.quantize(w, q4.INT4_ASYM, 32, out=q), 10)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    dt = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 10)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gt = timed(lambda: q4.gemm(x, q, out=y), 10)
+    flops = 2.0 * M * N * K
+    codec_bytes = N * K * 2 + q.nbytes()
+    return {
+        "gemm": {"shape": f"M={M} N={N} K={K} int4_asym g32 bf16", "ms": round(gt, 4),
+                 "TFLOPs": round(flops / (gt * 1e-3) / 1e12, 1),
+                 "pct_bf16_peak": round(100 * flops / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)},
+        "dequantize_14336x4096_asym_bf16": {"ms": round(dt, 4),
+                                             "GBps": round(codec_bytes / (dt * 1e-3) / 1e9, 1)},
+        "quantize_14336x4096_asym": {"ms": round(qt, 4),
+                                      "GBps": round(codec_bytes / (qt * 1e-3) / 1e9, 1)},
+    }
+
+
+def cpu_baseline(seconds: float):
+    """The C oracle (single thread) on the first decoder layer's matrices,
+    taken row by row until the time budget is spent: dequantize each weight
+    row to bf16 and form the fp64 product with x, as the reference does."""
+    import numpy as np
+    import oracle
+    from bit_group_wise_amd import synth
+
+    rows_done = 0
+    bytes_done = 0
+    t_total = 0.0
+    rng_x = {HID: synth.act_bits(1, HID, 5900, synth.BF16), FFN: synth.act_bits(1, FFN, 5901, synth.BF16)}
+    sample = []
+    for name, N, K, parts in LAYER_MATS:
+        for part, rows, idx in parts:
+            if t_total >= seconds:
+                break
+            w = synth.weight_f16_bits(rows, K, seed=5000 + idx)
+            codes, scales, _ = oracle.quantize(oracle.NF4, 64, w)
+            row_bytes = K // 2 + (K // 64) * 4
+            step = 64
+            for r0 in range(0, rows, step):
+                if t_total >= seconds:
+                    break
+                sel = np.arange(r0, min(r0 + step, rows), dtype=np.int64)
+                t = time.perf_counter()
+                oracle.matmul(oracle.NF4, 64, oracle.BF16, rng_x[K], codes, scales, None,
+                              rows, K, rows=sel)
+                t_total += time.perf_counter() - t
+                rows_done += sel.size
+                bytes_done += sel.size * row_bytes
+            sample.append(part)
+    return {
+        "value": round(bytes_done / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rows_done} weight rows of layer 0 ({', '.join(sample)}), NF4 g64, M=1 bf16: "
+                  f"dequantize + fp64 dot product, {t_total:.1f}s single-threaded",
+    }
+
+
+if __name__ == "__main__":
+    main()

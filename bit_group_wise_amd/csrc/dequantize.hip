@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__re
             if constexpr (FMT == Q4_NF4) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    v[i] = tbl[(cw[u] >> (4 * i)) & 0xf] * sc[u];
+                    v[i] = keep_f32(tbl[(cw[u] >> (4 * i)) & 0xf] * sc[u]);
             } else {
                 // spread nibbles into bytes: lo holds elements 0,2,4,6 and hi
                 // holds elements 1,3,5,7

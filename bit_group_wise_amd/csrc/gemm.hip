@@ -57,7 +57,7 @@ __device__ __forceinline__ void dequant32(const u32x4 &cw, float s, float zf, co
         if constexpr (FMT == Q4_NF4) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                v[i] = tbl[(w >> (4 * i)) & 0xf] * s;
+                v[i] = keep_f32(tbl[(w >> (4 * i)) & 0xf] * s);
         } else {
             const uint32_t lo = w & 0x0f0f0f0fu;
             const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;

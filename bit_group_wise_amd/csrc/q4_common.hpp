@@ -200,6 +200,16 @@ __device__ __forceinline__ uint32_t f2bf_bits(float f)
 {
     return std::bit_cast<uint16_t>((__bf16)f);
 }
+// Pins a binary32 value in a register.  Without it the compiler may fold
+// fp16(a * b) into one mixed-precision fma (v_fma_mixlo_f16) that rounds
+// the exact product once, instead of rounding to binary32 first and then to
+// fp16 as the dequantize rule states.  Emits no instruction.
+__device__ __forceinline__ float keep_f32(float v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // Byte I of a dword as a float (v_cvt_f32_ubyte{0..3}).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) { return (float)((v >> (8 * I)) & 0xffu); }
