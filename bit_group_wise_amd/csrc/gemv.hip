@@ -9,223 +9,568 @@
 // of packed codes and scales it streams.
 //
 // gfx950 mapping:
-//  * Each wave owns R rows; lane l streams 16-byte chunks c = l, l+64, ...
-//    (32 weights of each row, one dwordx4 load per row) and the matching
-//    activations (4 dwordx4 per row of x, shared by the R rows).
+//  * A wave owns one weight row at a time.  Along K it walks stages of
+//    64 lanes x 64 weights: lane l reads two 16-byte chunks of codes (buffer
+//    loads, so tails past a row or past the matrix read zeros).  The loads of
+//    the next positions -- of the same or the next row -- are issued before
+//    the current stage is computed, so HBM reads stay in flight.
 //  * The scale is hoisted out of the inner product: a chunk lies inside one
 //    group, so p = sum x * level is formed first and then acc += s * p
 //    (INT4-asym: acc += s * (p - z * sum x)).
 //  * Levels come from a per-workgroup LDS table indexed by a whole code byte:
-//    the entry holds the two nibbles' levels as a packed 16-bit pair, so one
-//    v_dot2_f32_{bf16,f16} multiplies two weights by two activations with an
-//    fp32 accumulator.  NF4 levels are split into hi + lo 16-bit parts (two
-//    dot2 per byte, about 17 significant bits); INT4 levels are exact.
-//  * The table is replicated for 32 lane slots at a 256-byte entry stride, so
-//    every lane reads its own bank (no conflicts), and the LDS address of a
-//    byte is formed by one v_perm_b32 (code byte -> address bits 8..15, lane
-//    slot -> bits 0..7).
-//  * Lane partial sums are reduced across the wave with shuffles; y is
-//    rounded once to the activation dtype.
+//    an entry holds the two nibbles' levels as a packed 16-bit pair, so one
+//    v_dot2_f32_{f16,bf16} multiplies two weights by two activations into an
+//    fp32 accumulator.  The table is replicated per lane (a lane reads only
+//    its own bank) and a byte's LDS address is one v_perm_b32 (code byte ->
+//    address bits 8..15, lane slot -> bits 0..7).
+//  * Level pairs: INT4 levels are small integers, exact in bf16 and fp16, so
+//    the activations are used as they are.  NF4 levels are taken in fp16; for
+//    bf16 activations with M <= 2 the activations are first converted to
+//    fp16 after an exact power-of-two scaling per row (max |x| mapped into
+//    [2^14, 2^15)), which is lossless over fp16's normal range.  For larger
+//    M with bf16 activations NF4 levels are split into bf16 hi + lo parts
+//    (two dot2 per byte).
+//  * Activations: for M = 1 and rows that fit one stage (K <= 4096) each lane
+//    keeps its slice in registers; else, for M <= 2, they are staged once per workgroup
+//    in LDS (rows padded to whole stages with zeros, 16 bytes of skew per 128
+//    so the 16-byte reads of a wave do not collide in banks); larger M reads
+//    them from L2 step by step.
+//  * Lane partial sums are reduced across the wave with DPP; y is rounded
+//    once to the activation dtype.
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 
 namespace q4 {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kBlock = kWaves * 64;
-constexpr int kTableDwords = 256 * 64;  // 256 entries x 256 bytes
+// Steps (of 8 weights) between scheduling barriers in a stage; 0 = none.
+#ifndef Q4_GEMV_SB
+#define Q4_GEMV_SB 2
+#endif
+// Positions (stages) whose loads are kept in flight per wave.
+#ifndef Q4_GEMV_DEPTH
+#define Q4_GEMV_DEPTH 2
+#endif
 
-__constant__ uint32_t c_parts[4][16] = {
+constexpr int kTableDwords = 256 * 64;  // 256 entries x 256 bytes = 64 KB
+constexpr int kXBytes = 56 * 1024;      // LDS region for staged activations
+constexpr int kStageChunks = 128;       // 16-byte chunks per row per stage
+constexpr int kStageXBytes = kStageChunks * 64;  // activation bytes per row per stage
+
+// Where a wave reads its activations from.
+enum XSrc { X_GLOBAL = 0, X_LDS = 1, X_REG = 2 };
+
+// Per-kernel arithmetic choices (see the header comment).
+template <int FMT, int ACT, int XS>
+struct Cfg {
+    // bf16 activations converted to fp16 for NF4 when they are staged
+    static constexpr bool conv_x = FMT == Q4_NF4 && ACT == Q4_BF16 && XS != X_GLOBAL;
+    // dot2 operand type
+    static constexpr int ct = (ACT == Q4_F16 || conv_x) ? Q4_F16 : Q4_BF16;
+    // NF4 in bf16: hi + lo level parts (two table dwords per byte)
+    static constexpr bool pair = FMT == Q4_NF4 && ct == Q4_BF16;
+};
+
+__constant__ uint32_t c_parts[3][16] = {
 #define ROW(a) {a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10], a[11], a[12], a[13], a[14], a[15]}
     ROW(kPairParts.nf4_bf16_hi), ROW(kPairParts.nf4_bf16_lo), ROW(kPairParts.nf4_f16_hi),
-    ROW(kPairParts.nf4_f16_lo),
 #undef ROW
 };
 
-template <int ACT>
+template <int CT>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
-    if constexpr (ACT == Q4_BF16)
+    if constexpr (CT == Q4_BF16)
         return __builtin_amdgcn_fdot2_f32_bf16(std::bit_cast<bf16x2>(a), std::bit_cast<bf16x2>(b), c,
                                                false);
     else
         return __builtin_amdgcn_fdot2(std::bit_cast<f16x2>(a), std::bit_cast<f16x2>(b), c, false);
 }
 
-template <int ACT>
+template <int CT>
 __device__ __forceinline__ uint32_t level_bits(int v)
 {
-    return ACT == Q4_BF16 ? f2bf_bits((float)v) : f2h_bits((float)v);
+    return CT == Q4_BF16 ? f2bf_bits((float)v) : f2h_bits((float)v);
 }
 
-// Fill the byte-indexed pair table: entry e, half h (0 = hi, 1 = lo), lane
-// slot L at byte offset e*256 + h*128 + 4L.
-template <int FMT, int ACT>
-__device__ __forceinline__ void fill_table(uint32_t *tbl)
+// The byte-indexed table.  Single layout: entry e, lane slot L (0..63) at
+// byte e*256 + 4L.  Pair layout (NF4 in bf16): hi part at e*256 + 4L, lo
+// part at e*256 + 128 + 4L, L in 0..31.  It is filled in 16-byte pieces:
+// thread t writes pieces t, t + BLOCK, ..., so each store instruction covers
+// consecutive addresses; a piece lies in one entry (half), so its dwords
+// are equal.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x)
 {
-    const int e = threadIdx.x >> 1;
-    const int h = threadIdx.x & 1;
-    const int n0 = e & 15, n1 = e >> 4;
-    uint32_t v;
-    if constexpr (FMT == Q4_NF4) {
-        const int part = (ACT == Q4_BF16 ? 0 : 2) + h;
-        v = c_parts[part][n0] | (c_parts[part][n1] << 16);
-    } else {
-        const int off = FMT == Q4_INT4_SYM ? 8 : 0;
-        v = h ? 0u : (level_bits<ACT>(n0 - off) | (level_bits<ACT>(n1 - off) << 16));
-    }
-    u32x4 *dst = (u32x4 *)(tbl + e * 64 + h * 32);
-    const u32x4 vv = {v, v, v, v};
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        dst[j] = vv;
+    return std::bit_cast<float>(
+        __builtin_amdgcn_update_dpp(0, std::bit_cast<int>(x), CTRL, ROW_MASK, 0xf, false));
 }
 
+// Sum over the 64 lanes with DPP row operations; the total is returned to
+// every lane (read from lane 63).
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        v += __shfl_xor(v, d);
+    v += dpp_f32<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141, 0xf>(v);  // row_half_mirror
+    v += dpp_f32<0x140, 0xf>(v);  // row_mirror: every lane holds its row's sum
+    v += dpp_f32<0x142, 0xa>(v);  // row_bcast15 into rows 1 and 3
+    v += dpp_f32<0x143, 0xc>(v);  // row_bcast31 into rows 2 and 3
+    return std::bit_cast<float>(__builtin_amdgcn_readlane(std::bit_cast<int>(v), 63));
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// (the hardware range check), so row and chunk tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+
+// Buffer views of the weight arrays starting at row n0.
+struct RowViews {
+    __amdgpu_buffer_rsrc_t codes, scales, zeros;
+    int zpar;  // parity of the row's first flat group index
+};
+
+template <int FMT>
+__device__ __forceinline__ RowViews row_views(const uint8_t *codes, const void *scales,
+                                              const uint8_t *zeros, int64_t n0, int64_t N,
+                                              int64_t row_bytes, int64_t G)
+{
+    constexpr int ss = FMT == Q4_NF4 ? 4 : 2;
+    RowViews v;
+    v.codes = make_rsrc(codes + n0 * row_bytes, (N - n0) * row_bytes);
+    v.scales = make_rsrc((const char *)scales + n0 * G * ss, (N - n0) * G * ss);
+    const int64_t g0 = n0 * G;
+    v.zpar = (int)(g0 & 1);
+    if constexpr (FMT == Q4_INT4_ASYM)
+        v.zeros = make_rsrc(zeros + (g0 >> 1), (N * G + 1) / 2 - (g0 >> 1));
+    else
+        v.zeros = v.codes;
     return v;
 }
 
-template <int FMT, int ACT, int MT, int R>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(const uint16_t *__restrict__ x, int M,
-                                                      const uint8_t *__restrict__ codes,
-                                                      const void *__restrict__ scales,
-                                                      const uint8_t *__restrict__ zeros, int N,
-                                                      int K, int gshift, uint16_t *__restrict__ y)
+// One pipeline stage of a wave: the 64 weights of lane unit u of one row
+// (two 16-byte chunks of codes) with their scales and zero-points.
+struct Stage {
+    u32x4 cw[2];
+    float sc[2];
+    float zf[2];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int unit, int gshift)
 {
-    __shared__ uint32_t tbl[kTableDwords];
-    fill_table<FMT, ACT>(tbl);
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    const uint32_t laneoff = (uint32_t)(lane & 31) << 2;
-    const int C = K >> 5;                 // 32-weight chunks per row
-    const int64_t G = (int64_t)(K >> gshift);  // groups per row
-    const int64_t row_bytes = K >> 1;
-    const int n_items = (N + R - 1) / R;
-    const int total_waves = gridDim.x * kWaves;
-    constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
-    const uint32_t ones = ACT == Q4_BF16 ? 0x3f803f80u : 0x3c003c00u;
-
-    for (int item = blockIdx.x * kWaves + (threadIdx.x >> 6); item < n_items; item += total_waves) {
-        const int n0 = item * R;
-        float acc[R][MT];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                acc[r][m] = 0.0f;
-
-        for (int c = lane; c < C; c += 64) {
-            u32x4 cw[R];
-            float sc[R];
-            float zf[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int row = n0 + r;
-                cw[r] = u32x4{0, 0, 0, 0};
-                sc[r] = 0.0f;
-                zf[r] = 0.0f;
-                if (row < N) {
-                    cw[r] = *(const u32x4 *)(codes + (int64_t)row * row_bytes + 16 * (int64_t)c);
-                    const int64_t gi = (int64_t)row * G + ((32 * c) >> gshift);
-                    if constexpr (FMT == Q4_NF4)
-                        sc[r] = ((const float *)scales)[gi];
-                    else
-                        sc[r] = h2f(((const uint16_t *)scales)[gi]);
-                    if constexpr (FMT == Q4_INT4_ASYM)
-                        zf[r] = (float)((zeros[gi >> 1] >> ((gi & 1) * 4)) & 0xf);
-                }
-            }
-            float p[R][MT];
-            float sx[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                sx[m] = 0.0f;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    p[r][m] = 0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x4 xv[MT];
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    xv[m] = u32x4{0, 0, 0, 0};
-                    if (m < M)
-                        xv[m] = *(const u32x4 *)(x + (int64_t)m * K + 32 * (int64_t)c + 8 * j);
-                }
-                if constexpr (FMT == Q4_INT4_ASYM) {
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            sx[m] = dot2<ACT>(xv[m][k], ones, sx[m]);
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t addr = __builtin_amdgcn_perm(cw[r][j], laneoff, kSel[k]);
-                        const uint32_t hi = *(const uint32_t *)((const char *)tbl + addr);
-                        uint32_t lo = 0;
-                        if constexpr (FMT == Q4_NF4)
-                            lo = *(const uint32_t *)((const char *)tbl + addr + 128);
-#pragma unroll
-                        for (int m = 0; m < MT; ++m) {
-                            p[r][m] = dot2<ACT>(xv[m][k], hi, p[r][m]);
-                            if constexpr (FMT == Q4_NF4)
-                                p[r][m] = dot2<ACT>(xv[m][k], lo, p[r][m]);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float t = p[r][m];
-                    if constexpr (FMT == Q4_INT4_ASYM)
-                        t = __builtin_fmaf(-zf[r], sx[m], t);
-                    acc[r][m] = __builtin_fmaf(t, sc[r], acc[r][m]);
-                }
-        }
-
-        float out = 0.0f;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float t = wave_sum(acc[r][m]);
-                if (lane == r * MT + m)
-                    out = t;
-            }
-        if (lane < R * MT) {
-            const int r = lane / MT, m = lane % MT;
-            if (m < M && n0 + r < N)
-                y[(int64_t)m * N + n0 + r] =
-                    (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+    for (int h = 0; h < 2; ++h) {
+        const int ch = 2 * unit + h;
+        // chunks past the row end read neighbouring (or out-of-range, hence
+        // zero) data; their activations are zero, so they add nothing
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, 16 * ch, 0, 0);
+        const int gl = (32 * ch) >> gshift;  // group index within the row
+        if constexpr (FMT == Q4_NF4)
+            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(v.scales, 4 * gl, 0, 0));
+        else
+            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, 2 * gl, 0, 0));
+        if constexpr (FMT == Q4_INT4_ASYM) {
+            const int gz = gl + v.zpar;
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, gz >> 1, 0, 0);
+            st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
+        } else {
+            st.zf[h] = 0.0f;
         }
     }
 }
 
-template <int FMT, int ACT, int MT, int R>
+// LDS byte offset of activation byte o of the staged rows: 16 bytes of skew
+// per 128 bytes, so 8 lanes reading 16 bytes 128 bytes apart hit 8 distinct
+// groups of 4 banks.
+__device__ __forceinline__ int xpad(int o) { return o + ((o >> 7) << 4); }
+
+// Activations of step (chunk ch, dword j) for rows m < MT.
+template <int MT, int XS>
+__device__ __forceinline__ void load_x(u32x4 (&xv)[MT], const uint32_t *xs,
+                                       __amdgpu_buffer_rsrc_t xr, int K, int xrow, int ch, int C,
+                                       int j)
+{
+    if constexpr (XS == X_LDS) {
+        // rows are zero past K, up to whole stages
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            xv[m] = *(const u32x4 *)((const char *)xs + xpad(m * xrow + 64 * ch + 16 * j));
+    } else {
+        // chunks past the row end are sent out of range, so they read zeros;
+        // rows m >= M lie past the end of the x view and read zeros too
+        const int base = ch < C ? 64 * ch + 16 * j : 0x7fffff00;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            xv[m] = __builtin_amdgcn_raw_buffer_load_b128(xr, base + m * 2 * K, 0, 0);
+    }
+}
+
+// Largest |value| of the two bf16 halves of a dword.
+__device__ __forceinline__ float bf2_absmax(uint32_t u)
+{
+    return fmaxf(fabsf(std::bit_cast<float>(u << 16)), fabsf(std::bit_cast<float>(u & 0xffff0000u)));
+}
+
+// Maximum over aligned groups of 8 lanes (returned to each lane of the group).
+__device__ __forceinline__ float max8(float v)
+{
+    v = fmaxf(v, dpp_f32<0xb1, 0xf>(v));   // lane ^ 1
+    v = fmaxf(v, dpp_f32<0x4e, 0xf>(v));   // lane ^ 2
+    v = fmaxf(v, dpp_f32<0x141, 0xf>(v));  // lane -> 7 - lane within 8
+    return v;
+}
+
+// Powers of two f = 2^(14 - e) and 1/f, e the exponent of a >= 0, so that
+// a * f lies in [2^14, 2^15) (clamped so both stay normal binary32).
+__device__ __forceinline__ void x_scale(float a, float &f, float &inv)
+{
+    const uint32_t b = std::bit_cast<uint32_t>(a);
+    int e = b ? (int)((b >> 23) & 0xff) - 127 : 14;
+    e = e < -100 ? -100 : e;
+    f = std::bit_cast<float>((uint32_t)(14 - e + 127) << 23);
+    inv = std::bit_cast<float>((uint32_t)(e - 14 + 127) << 23);
+}
+
+// bf16 pair -> fp16 pair after multiplying by the power of two f (exact over
+// fp16's normal range, nearest-even below it).
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u, float f)
+{
+    const float a = std::bit_cast<float>(u << 16) * f;
+    const float b = std::bit_cast<float>(u & 0xffff0000u) * f;
+    return pack_h2(a, b);
+}
+
+// Products of one stage: 8 steps of 8 weights (two chunks x four dwords of
+// codes).  Scheduling barriers every Q4_GEMV_SB steps keep the table reads of
+// later steps from being hoisted (which would exhaust the register budget).
+template <int FMT, int CT, bool PAIR, int MT, int XS>
+__device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
+                                              const uint32_t *__restrict__ tbl, const uint32_t *xs,
+                                              const u32x4 (&xreg)[XS == X_REG ? 8 * MT : 1],
+                                              const float (&xinv)[MT], __amdgpu_buffer_rsrc_t xr,
+                                              int K, int xrow, int unit, int C, uint32_t laneoff)
+{
+    constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
+    const uint32_t ones = CT == Q4_BF16 ? 0x3f803f80u : 0x3c003c00u;
+    // two independent accumulator chains per output (and two more for the lo
+    // parts), so consecutive dot2 do not wait on each other
+    constexpr int NA = MT <= 2 ? 2 : 1;
+    u32x4 xv[MT];
+    if constexpr (XS == X_REG) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            xv[m] = xreg[m * 8];
+    } else {
+        load_x<MT, XS>(xv, xs, xr, K, xrow, 2 * unit, C, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float p[MT][NA], pl[MT][NA];
+        float sx[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            sx[m] = 0.0f;
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+                p[m][a] = pl[m][a] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 xn[MT];
+            if (h * 4 + j < 7) {
+                if constexpr (XS == X_REG) {
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        xn[m] = xreg[m * 8 + h * 4 + j + 1];
+                } else {
+                    load_x<MT, XS>(xn, xs, xr, K, xrow, 2 * unit + (j == 3 ? h + 1 : h), C,
+                                   (j + 1) & 3);
+                }
+            }
+            if constexpr (FMT == Q4_INT4_ASYM) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        sx[m] = dot2<CT>(xv[m][k], ones, sx[m]);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t addr = __builtin_amdgcn_perm(st.cw[h][j], laneoff, kSel[k]);
+                const uint32_t lv = *(const uint32_t *)((const char *)tbl + addr);
+                uint32_t lo = 0;
+                if constexpr (PAIR)
+                    lo = *(const uint32_t *)((const char *)tbl + addr + 128);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    p[m][k % NA] = dot2<CT>(xv[m][k], lv, p[m][k % NA]);
+                    if constexpr (PAIR)
+                        pl[m][k % NA] = dot2<CT>(xv[m][k], lo, pl[m][k % NA]);
+                }
+            }
+            if (h * 4 + j < 7) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    xv[m] = xn[m];
+            }
+#if Q4_GEMV_SB > 0
+            if ((j + 1) % Q4_GEMV_SB == 0)
+                __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float t = 0.0f;
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+                t += PAIR ? p[m][a] + pl[m][a] : p[m][a];
+            if constexpr (FMT == Q4_INT4_ASYM)
+                t = __builtin_fmaf(-st.zf[h], sx[m], t);
+            acc[m] = __builtin_fmaf(t, st.sc[h] * xinv[m], acc[m]);
+        }
+    }
+}
+
+// Workgroup shape: 16 waves (one workgroup per CU, sharing one table and the
+// staged activations) when the activations are staged, else 8 waves (two
+// workgroups per CU).
+template <int XS>
+struct Shape {
+    static constexpr int waves = XS != X_GLOBAL ? 16 : 8;
+    static constexpr int block = waves * 64;
+    static constexpr int per_cu = XS != X_GLOBAL ? 1 : 2;
+};
+
+// A wave's position in its walk: row and stage along K.
+struct Pos {
+    int row, s;
+};
+
+// Each wave walks its rows and, inside a row, the stages along K.  The
+// loads of the next P positions are kept in flight in a ring of stage
+// registers: position q is computed while q+1..q+P-1 are arriving, and its
+// slot is refilled with position q+P right after.  The first P positions are
+// issued before the LDS is filled.
+template <int FMT, int ACT, int MT, int XS, int P>
+__global__ __launch_bounds__(Shape<XS>::block)
+__attribute__((amdgpu_waves_per_eu(XS != X_GLOBAL || MT < 8 ? 4 : 2)))
+void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+                 const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K,
+                 int gshift, uint16_t *__restrict__ y)
+{
+    using F = Cfg<FMT, ACT, XS>;
+    constexpr int kWaves = Shape<XS>::waves;
+    constexpr int kBlock = Shape<XS>::block;
+    __shared__ uint32_t tbl[kTableDwords];
+    __shared__ uint32_t xs[XS != X_GLOBAL ? kXBytes / 4 : 4];
+    // inverse activation scale of each staged 64-value unit
+    __shared__ float xsinv[XS != X_GLOBAL && Cfg<FMT, ACT, XS>::conv_x ? kXBytes / 128 : 1];
+
+    const int lane = threadIdx.x & 63;
+    const uint32_t laneoff = (uint32_t)(F::pair ? (lane & 31) : lane) << 2;
+    const int C = K >> 5;                                    // 16-byte chunks per row
+    const int S = (C + kStageChunks - 1) / kStageChunks;    // stages per row
+    const int G = K >> gshift;                               // groups per row
+    const int row_bytes = K >> 1;
+    const int xrow = S * kStageXBytes;                       // staged bytes per x row
+    const int total_waves = gridDim.x * kWaves;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)M * K * 2);
+
+    auto advance = [&](Pos q) {
+        if (++q.s == S) {
+            q.s = 0;
+            q.row += total_waves;
+        }
+        return q;
+    };
+
+    // Prologue, ordered so that nothing waits behind the weight stream
+    // (vector-memory loads retire in order): activations first, then the
+    // table's level values, then the first P weight positions.
+    u32x4 xreg[XS == X_REG ? 8 * MT : 1];
+    u32x4 xt[4];
+    int xp[4];
+    if constexpr (XS != X_GLOBAL) {
+        // the workgroup stages x once in LDS: row m at m * xrow, zero from
+        // byte 2K to the end of its last stage; at most 4 pieces of 16 bytes
+        // per thread
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = threadIdx.x + kBlock * i;
+            const int m = (16 * p) / xrow, o = 16 * p - m * xrow;
+            xp[i] = p < M * xrow / 16 ? p : -1;
+            xt[i] = u32x4{0, 0, 0, 0};
+            if (xp[i] >= 0 && o < 2 * K)
+                xt[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, m * 2 * K + o, 0, 0);
+        }
+    }
+    // NF4 level parts: lane i (mod 16) holds entry i; fetched by lane permutes
+    uint32_t part_lo = 0, part_hi = 0;
+    if constexpr (FMT == Q4_NF4) {
+        part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
+        if constexpr (F::pair)
+            part_hi = c_parts[1][lane & 15];
+    }
+
+    // ring of P in-flight positions (a row past the end has an empty view,
+    // so its loads return zeros and it is never computed)
+    Pos pos[P];
+    Stage st[P];
+    pos[0] = Pos{(int)__builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6)), 0};
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        if (q > 0)
+            pos[q] = advance(pos[q - 1]);
+        const RowViews v = row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
+        load_stage<FMT>(st[q], v, lane + 64 * pos[q].s, gshift);
+    }
+
+    // fp16 conversion of bf16 activations with a power-of-two scale per
+    // 64-value unit (one lane's share of a stage); the products are scaled
+    // back exactly together with the group scale
+    if constexpr (XS != X_GLOBAL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (F::conv_x) {
+                // the 8 pieces of a unit sit in 8 consecutive threads
+                float mx = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    mx = fmaxf(mx, bf2_absmax(xt[i][k]));
+                mx = max8(mx);
+                float f, inv;
+                x_scale(mx, f, inv);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    xt[i][k] = bf2_to_h2(xt[i][k], f);
+                if (xp[i] >= 0 && (xp[i] & 7) == 0)
+                    xsinv[xp[i] >> 3] = inv;
+            }
+            if (xp[i] >= 0)
+                *(u32x4 *)((char *)xs + xpad(16 * xp[i])) = xt[i];
+        }
+    }
+    // table: level values by lane permutes (NF4) or arithmetic (INT4)
+#pragma unroll
+    for (int i = 0; i < kTableDwords / 4 / kBlock; ++i) {
+        const int piece = threadIdx.x + kBlock * i;
+        const int e = piece >> 4, h = (piece >> 3) & 1;
+        const int n0 = e & 15, n1 = e >> 4;
+        uint32_t v;
+        if constexpr (FMT == Q4_NF4) {
+            // every lane holds the same part variable, so the permute reads
+            // entry n of that part; the hi/lo choice is made afterwards
+            uint32_t a = (uint32_t)__shfl((int)part_lo, n0), b = (uint32_t)__shfl((int)part_lo, n1);
+            if constexpr (F::pair) {
+                const uint32_t c = (uint32_t)__shfl((int)part_hi, n0);
+                const uint32_t d = (uint32_t)__shfl((int)part_hi, n1);
+                if (h) {
+                    a = c;
+                    b = d;
+                }
+            }
+            v = a | (b << 16);
+        } else {
+            const int off = FMT == Q4_INT4_SYM ? 8 : 0;
+            v = level_bits<F::ct>(n0 - off) | (level_bits<F::ct>(n1 - off) << 16);
+        }
+        ((u32x4 *)tbl)[piece] = u32x4{v, v, v, v};
+    }
+    __syncthreads();
+
+    // one stage per row (M = 1): each lane keeps its activation slice and
+    // its inverse scale in registers for the whole kernel
+    float xinv_reg[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        xinv_reg[m] = 1.0f;
+    if constexpr (XS == X_REG) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                xreg[m * 8 + t] = *(const u32x4 *)((const char *)xs +
+                                                   xpad(m * xrow + 64 * (2 * lane + (t >> 2)) +
+                                                        16 * (t & 3)));
+            if constexpr (F::conv_x)
+                xinv_reg[m] = xsinv[m * (xrow >> 7) + lane];
+        }
+    }
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        acc[m] = 0.0f;
+
+    while (pos[0].row < N) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const Pos cp = pos[q];
+            if (cp.row >= N)
+                break;
+            float xinv[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if constexpr (F::conv_x && XS == X_LDS)
+                    xinv[m] = xsinv[m * (xrow >> 7) + lane + 64 * cp.s];
+                else
+                    xinv[m] = xinv_reg[m];
+            }
+            compute_stage<FMT, F::ct, F::pair, MT, XS>(st[q], acc, tbl, xs, xreg, xinv, xr, K,
+                                                      xrow, lane + 64 * cp.s, C, laneoff);
+            // refill this slot with the position P steps ahead
+            pos[q] = advance(pos[(q + P - 1) % P]);
+            {
+                const RowViews v =
+                    row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
+                load_stage<FMT>(st[q], v, lane + 64 * pos[q].s, gshift);
+            }
+            if (cp.s == S - 1) {
+                float out = 0.0f;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float t = wave_sum(acc[m]);
+                    acc[m] = 0.0f;
+                    if (lane == m)
+                        out = t;
+                }
+                if (lane < M && lane < MT)
+                    y[(int64_t)lane * N + cp.row] =
+                        (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+            }
+        }
+    }
+}
+
+// Staged activations fit when M rows of whole stages, skewed, fit the region.
+bool x_fits_lds(int64_t M, int64_t K)
+{
+    const int64_t C = K / 32;
+    const int64_t S = (C + kStageChunks - 1) / kStageChunks;
+    const int64_t bytes = M * S * kStageXBytes;
+    return bytes + (bytes >> 3) + 16 <= kXBytes;
+}
+
+template <int FMT, int ACT, int MT, int XS>
 hipError_t launch_one(const void *x, int M, const uint8_t *codes, const void *scales,
                       const uint8_t *zeros, int64_t N, int64_t K, int gshift, void *y,
                       hipStream_t s)
 {
-    const int64_t n_items = (N + R - 1) / R;
-    int64_t blocks = (n_items + kWaves - 1) / kWaves;
-    const int64_t cap = (int64_t)device_cu_count() * 2;  // 64 KB of LDS each: 2 per CU
+    constexpr int waves = Shape<XS>::waves;
+    int64_t blocks = (N + waves - 1) / waves;
+    const int64_t cap = (int64_t)device_cu_count() * Shape<XS>::per_cu;
     if (blocks > cap)
         blocks = cap;
-    hipLaunchKernelGGL((gemv_kernel<FMT, ACT, MT, R>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                       (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
-                       (uint16_t *)y);
+    constexpr int depth = MT <= 2 ? Q4_GEMV_DEPTH : 2;
+    hipLaunchKernelGGL((gemv_kernel<FMT, ACT, MT, XS, depth>), dim3((unsigned)blocks),
+                       dim3(Shape<XS>::block), 0, s, (const uint16_t *)x, M, codes, scales, zeros,
+                       (int)N, (int)K, gshift, (uint16_t *)y);
     return hipGetLastError();
 }
 
@@ -233,15 +578,23 @@ template <int FMT, int ACT>
 hipError_t launch_m(const void *x, int M, const uint8_t *codes, const void *scales,
                     const uint8_t *zeros, int64_t N, int64_t K, int gshift, void *y, hipStream_t s)
 {
+    // M = 1 with one stage per row: activations live in registers; else
+    // (M <= 2) staged in LDS when they fit; else read from L2
+    const bool one_stage = K <= 32 * kStageChunks;
+    const bool xl = x_fits_lds(M <= 1 ? 1 : 2, K);
+#define Q4_GEMV_LAUNCH(MT_, XS_) \
+    launch_one<FMT, ACT, MT_, XS_>(x, M, codes, scales, zeros, N, K, gshift, y, s)
     if (M <= 1)
-        return launch_one<FMT, ACT, 1, 2>(x, M, codes, scales, zeros, N, K, gshift, y, s);
+        return one_stage ? Q4_GEMV_LAUNCH(1, X_REG)
+                         : (xl ? Q4_GEMV_LAUNCH(1, X_LDS) : Q4_GEMV_LAUNCH(1, X_GLOBAL));
     if (M <= 2)
-        return launch_one<FMT, ACT, 2, 2>(x, M, codes, scales, zeros, N, K, gshift, y, s);
+        return xl ? Q4_GEMV_LAUNCH(2, X_LDS) : Q4_GEMV_LAUNCH(2, X_GLOBAL);
     if (M <= 4)
-        return launch_one<FMT, ACT, 4, 2>(x, M, codes, scales, zeros, N, K, gshift, y, s);
+        return Q4_GEMV_LAUNCH(4, X_GLOBAL);
     if (M <= 8)
-        return launch_one<FMT, ACT, 8, 1>(x, M, codes, scales, zeros, N, K, gshift, y, s);
-    return launch_one<FMT, ACT, 16, 1>(x, M, codes, scales, zeros, N, K, gshift, y, s);
+        return Q4_GEMV_LAUNCH(8, X_GLOBAL);
+    return Q4_GEMV_LAUNCH(16, X_GLOBAL);
+#undef Q4_GEMV_LAUNCH
 }
 
 template <int FMT>
