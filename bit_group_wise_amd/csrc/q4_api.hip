@@ -46,11 +46,15 @@ size_t q4_codes_bytes(int64_t N, int64_t K)
     return (size_t)(N * K / 2);
 }
 
+// Scales and zero-points carry padding: the GEMM reads them with wide (up to
+// 16-byte, unaligned) loads that may run past the last entry into it.
+static size_t pad16(int64_t n) { return (size_t)q4::padded_meta_bytes(n); }
+
 size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g)
 {
     if (!format_ok(f) || !group_ok(g) || N <= 0 || K <= 0 || K % g != 0)
         return 0;
-    return (size_t)(N * (K / g)) * (f == Q4_NF4 ? 4u : 2u);
+    return pad16(N * (K / g) * (f == Q4_NF4 ? 4 : 2));
 }
 
 size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g)
@@ -59,7 +63,7 @@ size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g)
         return 0;
     if (f != Q4_INT4_ASYM)
         return 0;
-    return (size_t)((N * (K / g) + 1) / 2);
+    return pad16((N * (K / g) + 1) / 2);
 }
 
 const char *q4_status_str(q4_status s)
@@ -148,6 +152,8 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
     q4_status st = check_product(f, g, act_t, x, M, codes, scales, zeros, N, K, y);
     if (st != Q4_OK)
         return st;
+    if (K > Q4_GEMM_MAX_K)
+        return Q4_EUNSUPPORTED;
     return from_hip(q4::launch_gemm(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                     (hipStream_t)stream));
 }

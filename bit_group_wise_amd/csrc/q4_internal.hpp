@@ -13,6 +13,14 @@ namespace q4 {
 // Number of compute units of the current device (queried per call).
 int device_cu_count();
 
+// Allocated size of a scale or zero-point array of n meaningful bytes: at
+// least 16 bytes of padding, to a multiple of 16, so that loads of up to 16
+// bytes starting at any meaningful byte stay inside the allocation.
+__host__ __device__ constexpr int64_t padded_meta_bytes(int64_t n)
+{
+    return (n + 16 + 15) & ~(int64_t)15;
+}
+
 hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t K,
                            uint8_t *codes, void *scales, uint8_t *zeros, hipStream_t s);
 hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const void *scales,

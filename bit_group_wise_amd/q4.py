@@ -128,8 +128,11 @@ def alloc_quantized(fmt: int, g: int, N: int, K: int, device) -> QuantizedWeight
         raise Q4Error(EINVAL, "alloc_quantized")
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
     sdt = torch.float32 if fmt == NF4 else torch.float16
-    scales = torch.empty((N, K // g), dtype=sdt, device=device)
-    zeros = torch.empty((nz,), dtype=torch.uint8, device=device) if nz else None
+    # scale and zero-point storage carries the ABI's padding to 16 bytes;
+    # the tensors handed out are views of the meaningful leading part
+    es = 4 if fmt == NF4 else 2
+    scales = torch.zeros((ns // es,), dtype=sdt, device=device)[: N * (K // g)].view(N, K // g)
+    zeros = torch.zeros((nz,), dtype=torch.uint8, device=device)[: (N * (K // g) + 1) // 2] if nz else None
     return QuantizedWeight(fmt, g, N, K, codes, scales, zeros)
 
 

@@ -89,10 +89,14 @@ typedef enum {
 } q4_status;
 
 /* Sizes in bytes of the caller-allocated buffers for an [N, K] weight with
- * groups of g (0 for invalid arguments). */
+ * groups of g (0 for invalid arguments).  The scale and zero-point sizes
+ * include at least 16 bytes of trailing padding, rounded to a multiple of
+ * 16: q4_quantize writes only the leading entries (the padding stays as the
+ * caller left it) and no reader uses the padding as values, but q4_gemm's
+ * wide loads may read into it, so the whole size must be allocated. */
 size_t q4_codes_bytes(int64_t N, int64_t K);                      /* N*K/2 */
-size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4) */
-size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g);  /* asym: ceil(N*K/g / 2), else 0 */
+size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4), padded */
+size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g);  /* asym: ceil(N*K/g / 2), padded; else 0 */
 
 /* Quantize fp16 weights w[N, K] into codes, scales and (asym) zeros.
  * Sources: the coding rules above ("How 4-bit quantization works";
@@ -117,8 +121,11 @@ q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   int64_t N, int64_t K, void *y, void *stream);
 
 /* Prefill-shape product y[M, N] = x[M, K] . What^T for any M >= 1: weight
- * tiles are dequantized to the activation dtype in LDS and multiplied on the
- * matrix cores with fp32 accumulation; y is rounded once to act_t. */
+ * tiles are dequantized to the activation dtype on the fly (each value as
+ * q4_dequantize writes it) and multiplied on the matrix cores with fp32
+ * accumulation; y is rounded once to act_t ("Where the accuracy goes").
+ * K > Q4_GEMM_MAX_K returns Q4_EUNSUPPORTED. */
+#define Q4_GEMM_MAX_K 4194304
 q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
                   int64_t N, int64_t K, void *y, void *stream);

@@ -44,14 +44,15 @@ def test_size_helpers_reproduce_page_figures():
     n = so["params"]
     K = 4096
     N = n // K
+    # (the scale buffers carry 16 bytes of trailing padding, not counted)
     for g in (32, 64, 128):
-        mib = q4.scales_bytes(q4.INT4_SYM, N, K, g) / 2**20
+        mib = (q4.scales_bytes(q4.INT4_SYM, N, K, g) - 16) / 2**20
         assert mib == so["printed_mb"][str(g)]
     # 4 bits per weight: codes of 8B params are 4 GB (2^32 bytes)
     assert q4.codes_bytes(N, K) == n // 2
     # NF4 block 64 with 32-bit absmax: 0.5 extra bits per weight
     nb = fp["nf4_absmax_bits"]
-    extra_bits = q4.scales_bytes(q4.NF4, N, K, 64) * 8 / n
+    extra_bits = (q4.scales_bytes(q4.NF4, N, K, 64) - 16) * 8 / n
     assert extra_bits == nb["printed_bits"]
     # double quantisation figure (8-bit per block of 64 plus fp32 per 256 blocks)
     dq = nb["dq_bits"] / nb["block"] + 32 / (nb["block"] * nb["dq_block"])
@@ -77,7 +78,11 @@ def test_size_helpers_invalid():
     assert q4.scales_bytes(q4.NF4, 4, 100, 64) == 0
     assert q4.scales_bytes(7, 4, 128, 64) == 0
     assert q4.zeros_bytes(q4.NF4, 4, 128, 64) == 0
-    assert q4.zeros_bytes(q4.INT4_ASYM, 3, 96, 32) == (3 * 3 + 1) // 2
+    # padding: at least 16 bytes past the data, to a multiple of 16
+    # (9 groups -> 5 bytes of nibbles -> 32; 18 bytes of scales -> 48)
+    assert q4.zeros_bytes(q4.INT4_ASYM, 3, 96, 32) == 32
+    assert q4.scales_bytes(q4.INT4_SYM, 3, 96, 32) == 48
+    assert q4.scales_bytes(q4.NF4, 1, 128, 64) == 32
 
 
 # Fake device addresses: validation never dereferences them and returns
