@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--layers", type=int, default=LAYERS,
                    help="decoder layers in the weight stream (32 for the 7B shape)")
     p.add_argument("--no-graph", action="store_true", help="time plain stream launches only")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the CPU-oracle sample")
     p.add_argument("--skip-extra", action="store_true",
                    help="time only the decode token (for profiler runs)")
@@ -318,9 +318,12 @@ def extra_legs(torch, q4, dev, stream):
 
 
 def cpu_baseline(seconds: float):
-    """The C oracle (single thread) on the first decoder layer's matrices,
-    taken row by row until the time budget is spent: dequantize each weight
-    row to bf16 and form the fp64 product with x, as the reference does."""
+    """The C oracle (single thread) on the token's matrices, layer by layer
+    (the first 2048 rows of each), 64 rows at a time until the time budget
+    is spent: dequantize each weight row to bf16 and form the fp64 product
+    with x, as the reference does.  The weights are drawn with the same seeds
+    and distribution as the GPU run's (a different generator, so not the
+    same bits)."""
     import numpy as np
     import oracle
     from bit_group_wise_amd import synth
@@ -328,34 +331,39 @@ def cpu_baseline(seconds: float):
     rows_done = 0
     bytes_done = 0
     t_total = 0.0
-    rng_x = {HID: synth.act_bits(1, HID, 5900, synth.BF16), FFN: synth.act_bits(1, FFN, 5901, synth.BF16)}
-    sample = []
-    for name, N, K, parts in LAYER_MATS:
-        for part, rows, idx in parts:
-            if t_total >= seconds:
-                break
-            w = synth.weight_f16_bits(rows, K, seed=5000 + idx)
-            codes, scales, _ = oracle.quantize(oracle.NF4, 64, w)
-            row_bytes = K // 2 + (K // 64) * 4
-            step = 64
-            for r0 in range(0, rows, step):
+    xs = {HID: synth.act_bits(1, HID, 5900, synth.BF16), FFN: synth.act_bits(1, FFN, 5901, synth.BF16)}
+    mats = []
+    for layer in range(LAYERS):
+        for name, N, K, parts in LAYER_MATS:
+            for part, rows, idx in parts:
                 if t_total >= seconds:
                     break
-                sel = np.arange(r0, min(r0 + step, rows), dtype=np.int64)
-                t = time.perf_counter()
-                oracle.matmul(oracle.NF4, 64, oracle.BF16, rng_x[K], codes, scales, None,
-                              rows, K, rows=sel)
-                t_total += time.perf_counter() - t
-                rows_done += sel.size
-                bytes_done += sel.size * row_bytes
-            sample.append(part)
+                # the first 2048 rows of each matrix (a row-major draw, so
+                # these are the full matrix's first rows)
+                w = synth.weight_f16_bits(min(rows, 2048), K, seed=5000 + 7 * layer + idx)
+                rows = w.shape[0]
+                row_bytes = K // 2 + (K // 64) * 4
+                for r0 in range(0, rows, 64):
+                    if t_total >= seconds:
+                        break
+                    blk = w[r0:r0 + 64]
+                    codes, scales, _ = oracle.quantize(oracle.NF4, 64, blk)
+                    t = time.perf_counter()
+                    oracle.matmul(oracle.NF4, 64, oracle.BF16, xs[K], codes, scales, None,
+                                  blk.shape[0], K)
+                    t_total += time.perf_counter() - t
+                    rows_done += blk.shape[0]
+                    bytes_done += blk.shape[0] * row_bytes
+                mats.append(f"{part}{layer}")
+        if t_total >= seconds:
+            break
     return {
         "value": round(bytes_done / t_total / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{rows_done} weight rows of layer 0 ({', '.join(sample)}), NF4 g64, M=1 bf16: "
-                  f"dequantize + fp64 dot product, {t_total:.1f}s single-threaded",
+        "sample": f"{rows_done} weight rows (the first 2048 of each of {mats[0]} .. {mats[-1]}), "
+                  f"NF4 g64, M=1 bf16: dequantize + fp64 dot product, {t_total:.1f}s on one thread",
     }
 
 
