@@ -58,11 +58,38 @@ def parse():
                    help="time budget of the CPU-oracle sample")
     p.add_argument("--skip-extra", action="store_true",
                    help="time only the decode token (for profiler runs)")
+    p.add_argument("--only", choices=["gemm", "quantize", "dequantize", "copy"],
+                   help="run one leg alone, a few times, and print its timing "
+                        "(for profiler runs); 'copy' is a plain 1 GiB device copy, the "
+                        "reference for scaling HBM byte counters")
     return p.parse_args()
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when
+    the GEMV source has changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "gemv_nf4_decode_token_7b_traffic.md")
+    src = os.path.join(ROOT, "bit_group_wise_amd", "csrc", "gemv.hip")
+    try:
+        fields = {}
+        with open(prof) as f:
+            for line in f:
+                k, sep, v = line.strip().partition(": ")
+                if sep:
+                    fields[k] = v.strip()
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        if fields.get("gemv_source_sha256_16") != sha:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -80,6 +107,10 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     stream = torch.cuda.current_stream()
+
+    if args.only:
+        print(json.dumps(one_leg(args.only, torch, q4, dev, stream)), flush=True)
+        return
 
     # ---------------------------------------------------------- weights
     t0 = time.time()
@@ -270,23 +301,14 @@ def main():
             "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(gemv_avg_us, 3),
             "bytes_per_launch": round(w_bytes / n_launch),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 
 
-def extra_legs(torch, q4, dev, stream):
-    """Dequantize and prefill-GEMM legs on the INT4-asym g32 14336x4096 weight."""
-    N, K, M = 14336, 4096, 2048
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(401)
-    w = torch.empty((N, K), dtype=torch.float16, device=dev).normal_(0.001, 0.02, generator=gen)
-    gen.manual_seed(402)
-    x = torch.empty((M, K), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
-    x = x.to(torch.bfloat16)
-    q = q4.quantize(w, q4.INT4_ASYM, 32)
+def _timer(torch, stream):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(fn, reps):
@@ -298,7 +320,56 @@ def extra_legs(torch, q4, dev, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
+    return timed
 
+
+def _prefill_inputs(torch, q4, dev):
+    """The INT4-asym g32 14336x4096 weight (~ N(0.001, 0.02^2)) and the bf16
+    2048x4096 x (~ N(0, 1)) of the prefill workload, drawn on the GPU."""
+    N, K, M = 14336, 4096, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(401)
+    w = torch.empty((N, K), dtype=torch.float16, device=dev).normal_(0.001, 0.02, generator=gen)
+    gen.manual_seed(402)
+    x = torch.empty((M, K), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
+    return w, x.to(torch.bfloat16), q4.quantize(w, q4.INT4_ASYM, 32)
+
+
+def one_leg(leg, torch, q4, dev, stream):
+    """One leg alone, 5 timed repetitions (for profiler runs)."""
+    timed = _timer(torch, stream)
+    if leg == "copy":
+        n = 1 << 30
+        a = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        ms = timed(lambda: b.copy_(a), 5)
+        return {"leg": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+                "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    w, x, q = _prefill_inputs(torch, q4, dev)
+    N, K = w.shape
+    M = x.shape[0]
+    if leg == "quantize":
+        ms = timed(lambda: q4.quantize(w, q4.INT4_ASYM, 32, out=q), 5)
+        nb = N * K * 2 + q.nbytes()
+        return {"leg": leg, "ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    if leg == "dequantize":
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 5)
+        nb = N * K * 2 + q.nbytes()
+        return {"leg": leg, "ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: q4.gemm(x, q, out=y), 5)
+    return {"leg": "gemm", "ms": round(ms, 4),
+            "TFLOPs": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+
+
+def extra_legs(torch, q4, dev, stream):
+    """Quantize, dequantize and prefill-GEMM legs on the INT4-asym g32
+    14336x4096 weight."""
+    timed = _timer(torch, stream)
+    w, x, q = _prefill_inputs(torch, q4, dev)
+    N, K = w.shape
+    M = x.shape[0]
     qt = timed(lambda: q4.quantize(w, q4.INT4_ASYM, 32, out=q), 10)
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     dt = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 10)
