@@ -8,8 +8,14 @@ the bytes are those of the separate matrices), giving 4 GEMV launches per
 layer and 128 per token.
 
 One step = one decode token: the 128 dequant-GEMVs (M = 1, bf16 activations)
-over all 6,476,005,376 weights, replayed from a captured HIP graph.  `value`
-is the weight bytes (codes + absmax) streamed per token times tokens/s.
+over all 6,476,005,376 weights, run back to back as two chained launches of
+64 GEMVs (q4_gemv_chain: one persistent kernel per 64 products, the weight
+stream of the next product prefetched across the boundary).  The token's
+activations are fixed synthetic inputs, so the products are independent
+(Q4_TASK_NO_WAIT).  `value` is the weight bytes (codes + absmax) streamed per
+token times tokens/s.  Reported beside it: the same chain with a grid-wide
+wait before every product (each reading the previous outputs' memory order),
+and the 128 single-product q4_gemv launches replayed from a HIP graph.
 
 The same run also measures, each with HIP events on the launch stream:
   * the one-shot quantize of all weights (HBM-resident fp16 input),
@@ -53,7 +59,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--layers", type=int, default=LAYERS,
                    help="decoder layers in the weight stream (32 for the 7B shape)")
-    p.add_argument("--no-graph", action="store_true", help="time plain stream launches only")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replayed single-launch comparison")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the CPU-oracle sample")
     p.add_argument("--skip-extra", action="store_true",
@@ -70,11 +77,11 @@ def log(*a):
 
 
 def measured_traffic():
-    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None when
-    the GEMV source has changed since the counters were taken."""
+    """HBM bytes per chained-GEMV launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or
+    None when the GEMV source has changed since the counters were taken."""
     import hashlib
-    prof = os.path.join(ROOT, "profiles", "gemv_nf4_decode_token_7b_traffic.md")
+    prof = os.path.join(ROOT, "profiles", "gemv_chain_nf4_decode_token_7b_traffic.md")
     src = os.path.join(ROOT, "bit_group_wise_amd", "csrc", "gemv.hip")
     try:
         fields = {}
@@ -160,97 +167,88 @@ def main():
     xg.manual_seed(5901)
     x_f = torch.randn((1, FFN), generator=xg).to(torch.bfloat16).to(dev)
     outs = [[torch.empty((1, q.N), dtype=torch.bfloat16, device=dev) for q in row] for row in qw]
+    flat_q = [q for row in qw for q in row]
+    flat_y = [y for ys in outs for y in ys]
+    flat_x = [x_f if q.K == FFN else x_h for q in flat_q]
+    n_launch_gemv = len(flat_q)
+    sync = q4.chain_sync(dev)
 
-    def token():
-        for qs, ys in zip(qw, outs):
-            for (name, N, K, _), q, y in zip(LAYER_MATS, qs, ys):
-                q4.gemv(x_f if K == FFN else x_h, q, out=y)
+    def chains(flags):
+        tasks = [(x, q, y, flags) for x, q, y in zip(flat_x, flat_q, flat_y)]
+        return [tasks[i:i + q4.CHAIN_MAX] for i in range(0, len(tasks), q4.CHAIN_MAX)]
+    indep = chains(q4.TASK_NO_WAIT)
+    dep = chains(0)
+    n_chain = len(indep)
 
-    token()
+    def token_single():
+        for x, q, y in zip(flat_x, flat_q, flat_y):
+            q4.gemv(x, q, out=y)
+
+    def run_chains(cs):
+        for c in cs:
+            q4.gemv_chain(c, sync=sync)
+
+    # reference outputs: single-product launches; every chain must give the
+    # same bits
+    token_single()
     torch.cuda.synchronize()
-    eager_ref = [y.clone() for ys in outs for y in ys]
-
-    graph = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            token()                                # warm on the capture stream
-        stream.wait_stream(side)
+    ref = [y.clone() for y in flat_y]
+    for name, cs in (("independent", indep), ("dependent", dep)):
+        for y in flat_y:
+            y.zero_()
+        run_chains(cs)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            token()
-        torch.cuda.synchronize()
-        for rep in range(3):                       # replays must match eager
-            for ys in outs:
-                for y in ys:
-                    y.zero_()
-            graph.replay()
-            torch.cuda.synchronize()
-            flat = [y for ys in outs for y in ys]
-            if not all(torch.equal(a, b) for a, b in zip(flat, eager_ref)):
-                log("graph replay differs from eager launches: timing eager launches")
-                graph = None
-                break
+        if not all(torch.equal(a, b) for a, b in zip(flat_y, ref)):
+            raise RuntimeError(f"{name} chain differs from single-product launches")
+    if sync.cpu().tolist() != [0, 0, 0, 0]:
+        raise RuntimeError(f"chain sync words not clear: {sync.cpu().tolist()}")
 
-    def step():
-        if graph is not None:
-            graph.replay()
-        else:
-            token()
+    # each chained launch of the timed steps is bracketed by its own events
+    # on the launch stream (the kernel's average launch duration)
+    lev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in indep] for _ in range(args.steps)]
+
+    def step(evs=None):
+        for i, c in enumerate(indep):
+            if evs is not None:
+                evs[i][0].record(stream)
+            q4.gemv_chain(c, sync=sync)
+            if evs is not None:
+                evs[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     e0.record(stream)
     t_wall = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(lev[k])
     e1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms = e0.elapsed_time(e1) / args.steps
     value = w_bytes / (ms * 1e-3) / 1e9
 
-    # eager (no graph) rate for context
-    for _ in range(2):
-        token()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(max(args.steps // 5, 3)):
-        token()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / max(args.steps // 5, 3)
-
-    # per-launch GEMV durations (events around each launch on its stream)
-    ev = []
-    for qs, ys in zip(qw, outs):
-        for (name, N, K, _), q, y in zip(LAYER_MATS, qs, ys):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            q4.gemv(x_f if K == FFN else x_h, q, out=y)
-            b.record(stream)
-            ev.append((name, q.nbytes(), a, b))
-    torch.cuda.synchronize()
-    per = {}
-    tot_b = tot_ms = 0.0
-    for name, nb, a, b in ev:
-        d = a.elapsed_time(b)
-        per.setdefault(name, []).append((nb, d))
-        tot_b += nb
-        tot_ms += d
-    # roofline of the dominant kernel: average algorithmic bytes per GEMV
-    # launch over its average duration in the timed (graph-replayed) region
-    n_launch = sum(len(row) for row in qw)
-    gemv_avg_us = ms / n_launch * 1e3
-    gemv_gbs = (w_bytes / n_launch) / (gemv_avg_us * 1e-6) / 1e9
-    # (per-matrix event pairs around single launches also time the launch
-    # itself, so they read a little slower than the replayed stream)
-    per_kernel = {n: {"bytes": v[0][0], "avg_us_event": round(sum(d for _, d in v) / len(v) * 1e3, 2),
-                      "GBps_event": round(v[0][0] / (sum(d for _, d in v) / len(v) * 1e-3) / 1e9, 1)}
-                  for n, v in per.items()}
+    timed = _timer(torch, stream)
+    reps = max(args.steps // 5, 3)
+    dep_ms = timed(lambda: run_chains(dep), reps)
+    single_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            token_single()                         # warm on the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            token_single()
+        single_ms = timed(graph.replay, reps)
+        del graph
+    launch_ms = [a.elapsed_time(b) for evs in lev for a, b in evs]
+    chain_avg_us = sum(launch_ms) / len(launch_ms) * 1e3
+    bytes_per_chain = w_bytes / n_chain
+    chain_gbs = bytes_per_chain / (chain_avg_us * 1e-6) / 1e9
 
     extra = {}
     if not args.skip_extra:
@@ -280,12 +278,15 @@ def main():
                         + ("" if args.layers == LAYERS else f" ({args.layers} layers)"),
             "weights": n_weights,
             "weight_bytes_per_token": w_bytes,
-            "launch": "hip graph replay" if graph is not None else "stream launches",
+            "launch": f"{n_chain} chained launches of up to {q4.CHAIN_MAX} GEMVs "
+                      "(independent products)",
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-            "eager_ms_per_step": round(eager_ms, 4),
-            "eager_GBps": round(w_bytes / (eager_ms * 1e-3) / 1e9, 1),
             "wall_ms_per_step": round(wall_ms / args.steps, 4),
-            "gemv_per_matrix": per_kernel,
+            "dependent_chain_ms_per_step": round(dep_ms, 4),
+            "dependent_chain_GBps": round(w_bytes / (dep_ms * 1e-3) / 1e9, 1),
+            "single_launch_graph_ms_per_step": None if single_ms is None else round(single_ms, 4),
+            "single_launch_graph_GBps": None if single_ms is None
+            else round(w_bytes / (single_ms * 1e-3) / 1e9, 1),
             "quantize_all_ms": round(quant_ms, 3),
             "quantize_all_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
             "device": props.name,
@@ -294,13 +295,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<NF4, bf16, M=1>",
-            "achieved": round(gemv_gbs, 1),
+            "kernel": "gemv_chain_kernel<NF4, bf16> (64 GEMVs per launch)",
+            "achieved": round(chain_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
-            "avg_launch_us": round(gemv_avg_us, 3),
-            "bytes_per_launch": round(w_bytes / n_launch),
+            "frac": round(chain_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(chain_avg_us, 3),
+            "bytes_per_launch": round(bytes_per_chain),
+            "gemvs_per_launch": n_launch_gemv // n_chain,
             "traffic": measured_traffic(),
         },
         "cpu_baseline": cpu,

@@ -10,10 +10,13 @@
 //
 // gfx950 mapping:
 //  * A wave owns one weight row at a time.  Along K it walks stages of
-//    64 lanes x 64 weights: lane l reads two 16-byte chunks of codes (buffer
-//    loads, so tails past a row or past the matrix read zeros).  The loads of
-//    the next positions -- of the same or the next row -- are issued before
-//    the current stage is computed, so HBM reads stay in flight.
+//    128 chunks of 32 weights: lane l reads chunks l and 64 + l (16 bytes of
+//    codes each), so each load instruction of the wave covers 1 KB of
+//    consecutive bytes.  Loads are buffer loads (tails past a row or past the
+//    matrix read zeros) marked non-temporal, since every weight byte is used
+//    once.  The loads of the next positions -- of the same or the next row --
+//    are issued before the current stage is computed, so HBM reads stay in
+//    flight.
 //  * The scale is hoisted out of the inner product: a chunk lies inside one
 //    group, so p = sum x * level is formed first and then acc += s * p
 //    (INT4-asym: acc += s * (p - z * sum x)).
@@ -26,17 +29,19 @@
 //  * Level pairs: INT4 levels are small integers, exact in bf16 and fp16, so
 //    the activations are used as they are.  NF4 levels are taken in fp16; for
 //    bf16 activations with M <= 2 the activations are first converted to
-//    fp16 after an exact power-of-two scaling per row (max |x| mapped into
-//    [2^14, 2^15)), which is lossless over fp16's normal range.  For larger
-//    M with bf16 activations NF4 levels are split into bf16 hi + lo parts
-//    (two dot2 per byte).
+//    fp16 after an exact power-of-two scaling per 32-value chunk (max |x|
+//    mapped into [2^14, 2^15)), which is lossless over fp16's normal range.
+//    For larger M with bf16 activations NF4 levels are split into bf16 hi +
+//    lo parts (two dot2 per byte).
 //  * Activations: for M = 1 and rows that fit one stage (K <= 4096) each lane
-//    keeps its slice in registers; else, for M <= 2, they are staged once per workgroup
-//    in LDS (rows padded to whole stages with zeros, 16 bytes of skew per 128
-//    so the 16-byte reads of a wave do not collide in banks); larger M reads
-//    them from L2 step by step.
+//    keeps its slices in registers; else, for M <= 2, they are staged once
+//    per workgroup in LDS (rows padded to whole stages with zeros, 16 bytes
+//    of skew per 64-byte chunk so the 16-byte reads of a wave do not collide
+//    in banks); larger M reads them from L2 step by step.
 //  * Lane partial sums are reduced across the wave with DPP; y is rounded
 //    once to the activation dtype.
+#include <type_traits>
+
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 
@@ -47,13 +52,17 @@ namespace {
 #ifndef Q4_GEMV_SB
 #define Q4_GEMV_SB 2
 #endif
-// Positions (stages) whose loads are kept in flight per wave.
+// Positions (stages) whose loads are kept in flight per wave, in the
+// single-product and the chained kernels.
 #ifndef Q4_GEMV_DEPTH
 #define Q4_GEMV_DEPTH 2
 #endif
+#ifndef Q4_GEMV_CHAIN_DEPTH
+#define Q4_GEMV_CHAIN_DEPTH 2
+#endif
 
 constexpr int kTableDwords = 256 * 64;  // 256 entries x 256 bytes = 64 KB
-constexpr int kXBytes = 56 * 1024;      // LDS region for staged activations
+constexpr int kXBytes = 80 * 1024;      // LDS region for staged activations
 constexpr int kStageChunks = 128;       // 16-byte chunks per row per stage
 constexpr int kStageXBytes = kStageChunks * 64;  // activation bytes per row per stage
 
@@ -153,31 +162,40 @@ __device__ __forceinline__ RowViews row_views(const uint8_t *codes, const void *
     return v;
 }
 
-// One pipeline stage of a wave: the 64 weights of lane unit u of one row
-// (two 16-byte chunks of codes) with their scales and zero-points.
+// One pipeline stage of a wave: 128 chunks of 32 weights of one row; lane l
+// holds chunks l and 64 + l of the stage (so each of the two 16-byte loads
+// of the wave reads 1 KB of consecutive codes), with their scales and
+// zero-points.
 struct Stage {
     u32x4 cw[2];
     float sc[2];
     float zf[2];
 };
 
+// Chunk of half h of stage s for a lane.
+__device__ __forceinline__ int stage_chunk(int s, int lane, int h) { return kStageChunks * s + 64 * h + lane; }
+
+// Non-temporal loads: the weights are streamed once per product, so they are
+// not kept in the caches (the "nt" cache-policy bit).
+constexpr int kNT = 2;
+
 template <int FMT>
-__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int unit, int gshift)
+__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, int lane, int gshift)
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int ch = 2 * unit + h;
+        const int ch = stage_chunk(s, lane, h);
         // chunks past the row end read neighbouring (or out-of-range, hence
         // zero) data; their activations are zero, so they add nothing
-        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, 16 * ch, 0, 0);
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, 16 * ch, 0, kNT);
         const int gl = (32 * ch) >> gshift;  // group index within the row
         if constexpr (FMT == Q4_NF4)
-            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(v.scales, 4 * gl, 0, 0));
+            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(v.scales, 4 * gl, 0, kNT));
         else
-            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, 2 * gl, 0, 0));
+            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, 2 * gl, 0, kNT));
         if constexpr (FMT == Q4_INT4_ASYM) {
             const int gz = gl + v.zpar;
-            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, gz >> 1, 0, 0);
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, gz >> 1, 0, kNT);
             st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
         } else {
             st.zf[h] = 0.0f;
@@ -186,9 +204,9 @@ __device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int uni
 }
 
 // LDS byte offset of activation byte o of the staged rows: 16 bytes of skew
-// per 128 bytes, so 8 lanes reading 16 bytes 128 bytes apart hit 8 distinct
-// groups of 4 banks.
-__device__ __forceinline__ int xpad(int o) { return o + ((o >> 7) << 4); }
+// per 64-byte chunk, so the 16 lanes of a read pass (16-byte reads, one
+// chunk apart) fall on 16 distinct groups of 4 banks (offsets 80 l mod 256).
+__device__ __forceinline__ int xpad(int o) { return o + ((o >> 6) << 4); }
 
 // Activations of step (chunk ch, dword j) for rows m < MT.
 template <int MT, int XS>
@@ -217,12 +235,11 @@ __device__ __forceinline__ float bf2_absmax(uint32_t u)
     return fmaxf(fabsf(std::bit_cast<float>(u << 16)), fabsf(std::bit_cast<float>(u & 0xffff0000u)));
 }
 
-// Maximum over aligned groups of 8 lanes (returned to each lane of the group).
-__device__ __forceinline__ float max8(float v)
+// Maximum over aligned groups of 4 lanes (returned to each lane of the group).
+__device__ __forceinline__ float max4(float v)
 {
-    v = fmaxf(v, dpp_f32<0xb1, 0xf>(v));   // lane ^ 1
-    v = fmaxf(v, dpp_f32<0x4e, 0xf>(v));   // lane ^ 2
-    v = fmaxf(v, dpp_f32<0x141, 0xf>(v));  // lane -> 7 - lane within 8
+    v = fmaxf(v, dpp_f32<0xb1, 0xf>(v));  // lane ^ 1
+    v = fmaxf(v, dpp_f32<0x4e, 0xf>(v));  // lane ^ 2
     return v;
 }
 
@@ -253,8 +270,9 @@ template <int FMT, int CT, bool PAIR, int MT, int XS>
 __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                                               const uint32_t *__restrict__ tbl, const uint32_t *xs,
                                               const u32x4 (&xreg)[XS == X_REG ? 8 * MT : 1],
-                                              const float (&xinv)[MT], __amdgpu_buffer_rsrc_t xr,
-                                              int K, int xrow, int unit, int C, uint32_t laneoff)
+                                              const float (&xinv)[MT][2], __amdgpu_buffer_rsrc_t xr,
+                                              int K, int xrow, int s, int lane, int C,
+                                              uint32_t laneoff)
 {
     constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
     const uint32_t ones = CT == Q4_BF16 ? 0x3f803f80u : 0x3c003c00u;
@@ -267,7 +285,7 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
         for (int m = 0; m < MT; ++m)
             xv[m] = xreg[m * 8];
     } else {
-        load_x<MT, XS>(xv, xs, xr, K, xrow, 2 * unit, C, 0);
+        load_x<MT, XS>(xv, xs, xr, K, xrow, stage_chunk(s, lane, 0), C, 0);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -289,8 +307,8 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                     for (int m = 0; m < MT; ++m)
                         xn[m] = xreg[m * 8 + h * 4 + j + 1];
                 } else {
-                    load_x<MT, XS>(xn, xs, xr, K, xrow, 2 * unit + (j == 3 ? h + 1 : h), C,
-                                   (j + 1) & 3);
+                    load_x<MT, XS>(xn, xs, xr, K, xrow, stage_chunk(s, lane, j == 3 ? h + 1 : h),
+                                   C, (j + 1) & 3);
                 }
             }
             if constexpr (FMT == Q4_INT4_ASYM) {
@@ -332,7 +350,7 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                 t += PAIR ? p[m][a] + pl[m][a] : p[m][a];
             if constexpr (FMT == Q4_INT4_ASYM)
                 t = __builtin_fmaf(-st.zf[h], sx[m], t);
-            acc[m] = __builtin_fmaf(t, st.sc[h] * xinv[m], acc[m]);
+            acc[m] = __builtin_fmaf(t, st.sc[h] * xinv[m][h], acc[m]);
         }
     }
 }
@@ -340,11 +358,16 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
 // Workgroup shape: 16 waves (one workgroup per CU, sharing one table and the
 // staged activations) when the activations are staged, else 8 waves (two
 // workgroups per CU).
+#ifndef Q4_GEMV_STAGED_WAVES
+#define Q4_GEMV_STAGED_WAVES 16
+#endif
 template <int XS>
 struct Shape {
-    static constexpr int waves = XS != X_GLOBAL ? 16 : 8;
+    static constexpr int waves = XS != X_GLOBAL ? Q4_GEMV_STAGED_WAVES : 8;
     static constexpr int block = waves * 64;
     static constexpr int per_cu = XS != X_GLOBAL ? 1 : 2;
+    // pieces of 16 bytes per thread that cover the staged-activation region
+    static constexpr int x_pieces = (kXBytes / 16 + block - 1) / block;
 };
 
 // A wave's position in its walk: row and stage along K.
@@ -359,7 +382,7 @@ struct Pos {
 // issued before the LDS is filled.
 template <int FMT, int ACT, int MT, int XS, int P>
 __global__ __launch_bounds__(Shape<XS>::block)
-__attribute__((amdgpu_waves_per_eu(XS != X_GLOBAL || MT < 8 ? 4 : 2)))
+__attribute__((amdgpu_waves_per_eu(XS != X_GLOBAL ? Shape<XS>::waves / 4 : (MT < 8 ? 4 : 2))))
 void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
                  const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K,
                  int gshift, uint16_t *__restrict__ y)
@@ -367,10 +390,18 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     using F = Cfg<FMT, ACT, XS>;
     constexpr int kWaves = Shape<XS>::waves;
     constexpr int kBlock = Shape<XS>::block;
-    __shared__ uint32_t tbl[kTableDwords];
-    __shared__ uint32_t xs[XS != X_GLOBAL ? kXBytes / 4 : 4];
-    // inverse activation scale of each staged 64-value unit
-    __shared__ float xsinv[XS != X_GLOBAL && Cfg<FMT, ACT, XS>::conv_x ? kXBytes / 128 : 1];
+    // One LDS block with the table first, at address 0, so that a lookup's
+    // address is the v_perm result itself.
+    struct Lds {
+        uint32_t tbl[kTableDwords];
+        uint32_t xs[XS != X_GLOBAL ? kXBytes / 4 : 4];
+        // inverse activation scale of each staged 32-value chunk
+        float xsinv[XS != X_GLOBAL && Cfg<FMT, ACT, XS>::conv_x ? kXBytes / 64 : 1];
+    };
+    __shared__ Lds lds;
+    uint32_t *const tbl = lds.tbl;
+    uint32_t *const xs = lds.xs;
+    float *const xsinv = lds.xsinv;
 
     const int lane = threadIdx.x & 63;
     const uint32_t laneoff = (uint32_t)(F::pair ? (lane & 31) : lane) << 2;
@@ -394,14 +425,14 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     // (vector-memory loads retire in order): activations first, then the
     // table's level values, then the first P weight positions.
     u32x4 xreg[XS == X_REG ? 8 * MT : 1];
-    u32x4 xt[4];
-    int xp[4];
+    constexpr int XP = Shape<XS>::x_pieces;
+    u32x4 xt[XP];
+    int xp[XP];
     if constexpr (XS != X_GLOBAL) {
         // the workgroup stages x once in LDS: row m at m * xrow, zero from
-        // byte 2K to the end of its last stage; at most 4 pieces of 16 bytes
-        // per thread
+        // byte 2K to the end of its last stage, in pieces of 16 bytes
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < XP; ++i) {
             const int p = threadIdx.x + kBlock * i;
             const int m = (16 * p) / xrow, o = 16 * p - m * xrow;
             xp[i] = p < M * xrow / 16 ? p : -1;
@@ -428,29 +459,29 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
         if (q > 0)
             pos[q] = advance(pos[q - 1]);
         const RowViews v = row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-        load_stage<FMT>(st[q], v, lane + 64 * pos[q].s, gshift);
+        load_stage<FMT>(st[q], v, pos[q].s, lane, gshift);
     }
 
     // fp16 conversion of bf16 activations with a power-of-two scale per
-    // 64-value unit (one lane's share of a stage); the products are scaled
-    // back exactly together with the group scale
+    // 32-value chunk (half of a lane's share of a stage); the products are
+    // scaled back exactly together with the group scale
     if constexpr (XS != X_GLOBAL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < XP; ++i) {
             if constexpr (F::conv_x) {
-                // the 8 pieces of a unit sit in 8 consecutive threads
+                // the 4 pieces of a chunk sit in 4 consecutive threads
                 float mx = 0.0f;
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     mx = fmaxf(mx, bf2_absmax(xt[i][k]));
-                mx = max8(mx);
+                mx = max4(mx);
                 float f, inv;
                 x_scale(mx, f, inv);
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     xt[i][k] = bf2_to_h2(xt[i][k], f);
-                if (xp[i] >= 0 && (xp[i] & 7) == 0)
-                    xsinv[xp[i] >> 3] = inv;
+                if (xp[i] >= 0 && (xp[i] & 3) == 0)
+                    xsinv[xp[i] >> 2] = inv;
             }
             if (xp[i] >= 0)
                 *(u32x4 *)((char *)xs + xpad(16 * xp[i])) = xt[i];
@@ -484,22 +515,25 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     }
     __syncthreads();
 
-    // one stage per row (M = 1): each lane keeps its activation slice and
-    // its inverse scale in registers for the whole kernel
-    float xinv_reg[MT];
+    // one stage per row (M = 1): each lane keeps its activation slices
+    // (chunks lane and 64 + lane) and their inverse scales in registers for
+    // the whole kernel
+    float xinv_reg[MT][2];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-        xinv_reg[m] = 1.0f;
+        xinv_reg[m][0] = xinv_reg[m][1] = 1.0f;
     if constexpr (XS == X_REG) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 xreg[m * 8 + t] = *(const u32x4 *)((const char *)xs +
-                                                   xpad(m * xrow + 64 * (2 * lane + (t >> 2)) +
+                                                   xpad(m * xrow + 64 * stage_chunk(0, lane, t >> 2) +
                                                         16 * (t & 3)));
-            if constexpr (F::conv_x)
-                xinv_reg[m] = xsinv[m * (xrow >> 7) + lane];
+            if constexpr (F::conv_x) {
+                xinv_reg[m][0] = xsinv[m * (xrow >> 6) + stage_chunk(0, lane, 0)];
+                xinv_reg[m][1] = xsinv[m * (xrow >> 6) + stage_chunk(0, lane, 1)];
+            }
         }
     }
 
@@ -508,28 +542,33 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     for (int m = 0; m < MT; ++m)
         acc[m] = 0.0f;
 
+    // A round of the ring is never left in the middle (the load waits stay
+    // partial only if every path refills every slot): a position past the
+    // last row has loaded zeros from an empty view; it is computed on them
+    // and writes nothing.
     while (pos[0].row < N) {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const Pos cp = pos[q];
-            if (cp.row >= N)
-                break;
-            float xinv[MT];
+            float xinv[MT][2];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if constexpr (F::conv_x && XS == X_LDS)
-                    xinv[m] = xsinv[m * (xrow >> 7) + lane + 64 * cp.s];
-                else
-                    xinv[m] = xinv_reg[m];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if constexpr (F::conv_x && XS == X_LDS)
+                        xinv[m][h] = xsinv[m * (xrow >> 6) + stage_chunk(cp.s, lane, h)];
+                    else
+                        xinv[m][h] = xinv_reg[m][h];
+                }
             }
             compute_stage<FMT, F::ct, F::pair, MT, XS>(st[q], acc, tbl, xs, xreg, xinv, xr, K,
-                                                      xrow, lane + 64 * cp.s, C, laneoff);
+                                                      xrow, cp.s, lane, C, laneoff);
             // refill this slot with the position P steps ahead
             pos[q] = advance(pos[(q + P - 1) % P]);
             {
                 const RowViews v =
                     row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-                load_stage<FMT>(st[q], v, lane + 64 * pos[q].s, gshift);
+                load_stage<FMT>(st[q], v, pos[q].s, lane, gshift);
             }
             if (cp.s == S - 1) {
                 float out = 0.0f;
@@ -540,7 +579,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                     if (lane == m)
                         out = t;
                 }
-                if (lane < M && lane < MT)
+                if (cp.row < N && lane < M && lane < MT)
                     y[(int64_t)lane * N + cp.row] =
                         (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
             }
@@ -548,13 +587,387 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     }
 }
 
-// Staged activations fit when M rows of whole stages, skewed, fit the region.
+// ---------------------------------------------------------------------------
+// Chained GEMVs: one persistent launch runs a list of M = 1 GEMVs in order.
+//
+// The weights never depend on earlier tasks, so each compute wave's ring of
+// in-flight weight loads runs on across task boundaries.  Only x may depend
+// on earlier tasks.  A workgroup is 15 compute waves and one loader wave.
+// x sits in LDS, double-buffered, as loaded (linear); each lane of a compute
+// wave converts its own chunks in registers, as the single-product kernels
+// do when staging.  The loader copies x of task t in by LDS-DMA once every
+// compute wave has entered task t - 1 (so the buffer's previous task is
+// done), waits for it (it has no weight loads to drain) and publishes it; a
+// compute wave entering task t waits only for that.  For a task that reads
+// earlier outputs the loader first waits until every compute wave has
+// finished the earlier tasks, then for the whole grid (a grid barrier
+// between loader waves).  The compute waves never wait for each other.  The
+// table is filled once per launch.
+struct ChainTask {
+    const uint16_t *x;
+    const uint8_t *codes;
+    const void *scales;
+    const uint8_t *zeros;
+    uint16_t *y;
+    int N, K;
+    int wait;  // 1: wait for every earlier task before reading x
+};
+constexpr int kChainMax = Q4_GEMV_CHAIN_MAX;
+struct ChainArgs {
+    ChainTask t[kChainMax];
+    int ntasks;
+    int gshift;
+    // [0] barrier arrivals and [1] finished workgroups (zero on entry, left
+    // zero on exit); [2] set to 1 when a barrier wait ran out
+    uint32_t *sync;
+};
+constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a second)
+constexpr int kChainMaxK = 16384;
+constexpr int kChainLinBytes = 2 * kChainMaxK;  // one buffer of x as loaded
+
+// A wave's position in the chain: task, row and stage along K.
+struct CPos {
+    int t, row, s;
+};
+
+__device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
+
+// s_waitcnt on vector memory only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A lane's x slice for stage s of a row: chunks l and 64 + l of the stage,
+// from LDS (zero past K), with the inverse scales of their conversion.
+__device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2], const char *lin,
+                                              const float *inv, int s, int lane, int C)
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ch = stage_chunk(s, lane, h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xreg[4 * h + j] = ch < C ? *(const u32x4 *)(lin + 64 * ch + 16 * j) : u32x4{0, 0, 0, 0};
+        xinv[h] = ch < C ? inv[ch] : 1.0f;
+    }
+}
+
+// In-place conversion of x (linear, C chunks) where the arithmetic uses fp16
+// for bf16 activations: per 32-value chunk, max |x| scaled into
+// [2^14, 2^15) by a power of two (the staged single-product conversion);
+// inv receives the chunks' inverse scales (1 when nothing is converted).
+template <int FMT, int ACT>
+__device__ __forceinline__ void chain_convert_x(char *lin, float *inv, int C, int lane)
+{
+    using F = Cfg<FMT, ACT, X_LDS>;
+    for (int ch = lane; ch < C; ch += 64) {
+        if constexpr (F::conv_x) {
+            u32x4 v[4];
+            float mx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = *(const u32x4 *)(lin + 64 * ch + 16 * j);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    mx = fmaxf(mx, bf2_absmax(v[j][k]));
+            }
+            float f, iv;
+            x_scale(mx, f, iv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[j][k] = bf2_to_h2(v[j][k], f);
+                *(u32x4 *)(lin + 64 * ch + 16 * j) = v[j];
+            }
+            inv[ch] = iv;
+        } else {
+            inv[ch] = 1.0f;
+        }
+    }
+}
+
+constexpr int kChainCompute = 15;  // compute waves per workgroup (wave 15 loads x)
+
+// DEP: some task waits for earlier outputs (else the grid-barrier code is
+// left out).
+template <int FMT, int ACT, int P, bool DEP>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_chain_kernel(const ChainArgs a)
+{
+    using F = Cfg<FMT, ACT, X_LDS>;  // the arithmetic of the staged single-product kernels
+    static_assert(Cfg<FMT, ACT, X_REG>::ct == F::ct && Cfg<FMT, ACT, X_REG>::pair == F::pair,
+                  "x source must not change the arithmetic");
+    // One LDS block with the table first, at address 0, so that a lookup's
+    // address is the v_perm result itself.
+    struct Lds {
+        uint32_t tbl[kTableDwords];
+        char lin[2][kChainLinBytes];
+        float xinv[2][kChainMaxK / 32];
+        int entered[2];  // compute waves that entered tasks of each parity (cumulative)
+        int ready[2];    // the task whose x lin[parity] holds
+    };
+    __shared__ Lds lds;
+    uint32_t *const tbl = lds.tbl;
+    auto &lin = lds.lin;
+    auto &xinv_lds = lds.xinv;
+    auto &entered = lds.entered;
+    auto &ready = lds.ready;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t laneoff = (uint32_t)(F::pair ? (lane & 31) : lane) << 2;
+    const int nt = a.ntasks;
+    // every compute wave has entered task t
+    auto all_entered = [&](int t) {
+        return __hip_atomic_load(&entered[t & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
+               kChainCompute * (t / 2 + 1);
+    };
+    auto fail = [&]() { __hip_atomic_store(&a.sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+
+    // the level table, by every wave
+    {
+        uint32_t part_lo = 0, part_hi = 0;
+        if constexpr (FMT == Q4_NF4) {
+            part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
+            if constexpr (F::pair)
+                part_hi = c_parts[1][lane & 15];
+        }
+#pragma unroll
+        for (int i = 0; i < kTableDwords / 4 / 1024; ++i) {
+            const int piece = threadIdx.x + 1024 * i;
+            const int e = piece >> 4, h = (piece >> 3) & 1;
+            const int n0 = e & 15, n1 = e >> 4;
+            uint32_t v;
+            if constexpr (FMT == Q4_NF4) {
+                uint32_t x0 = (uint32_t)__shfl((int)part_lo, n0), x1 = (uint32_t)__shfl((int)part_lo, n1);
+                if constexpr (F::pair) {
+                    const uint32_t c0 = (uint32_t)__shfl((int)part_hi, n0);
+                    const uint32_t c1 = (uint32_t)__shfl((int)part_hi, n1);
+                    if (h) {
+                        x0 = c0;
+                        x1 = c1;
+                    }
+                }
+                v = x0 | (x1 << 16);
+            } else {
+                const int off = FMT == Q4_INT4_SYM ? 8 : 0;
+                v = level_bits<F::ct>(n0 - off) | (level_bits<F::ct>(n1 - off) << 16);
+            }
+            ((u32x4 *)tbl)[piece] = u32x4{v, v, v, v};
+        }
+    }
+
+    if (wave == kChainCompute) {
+        // ---------------------------------------------------------- loader
+        auto copy_x = [&](int t) {
+            const ChainTask &T = a.t[t];
+            const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
+            const int n1k = (2 * T.K + 1023) >> 10;
+            char *dst = lin[t & 1];
+            for (int b = 0; b < n1k; ++b)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (__attribute__((address_space(3))) void *)(dst + 1024 * b), 16, 16 * lane,
+                    1024 * b, 0, 0);
+            wait_vm<0>();
+            chain_convert_x<FMT, ACT>(dst, xinv_lds[t & 1], T.K >> 5, lane);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the converted x is in LDS
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __hip_atomic_store(&ready[t & 1], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
+        if (lane == 0) {
+            entered[0] = kChainCompute;  // task 0 is entered by every compute wave in the prologue
+            entered[1] = 0;
+            ready[0] = ready[1] = -1;
+        }
+        copy_x(0);
+        __syncthreads();  // the table, the counters and x of task 0
+        int nbar = 0;
+        for (int t = 1; t < nt; ++t) {
+            // lin[t & 1] held x of task t - 2: wait until every compute wave
+            // has entered t - 1; a task that reads earlier outputs waits
+            // until they have finished t - 1 (entered t, stores complete)
+            const bool wait = DEP && a.t[t].wait;
+            const int need = wait ? t : t - 1;
+            uint32_t spins = 0;
+            while (!all_entered(need)) {
+                if (++spins == kSpinLimit) {
+                    fail();
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (wait) {
+                // grid barrier between the loaders: this workgroup's
+                // outputs are released with the arrival, the others'
+                // acquired after it
+                ++nbar;
+                if (lane == 0) {
+                    __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t target = (uint32_t)nbar * gridDim.x;
+                    uint32_t gspins = 0;
+                    while (__hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                           target) {
+                        if (++gspins == kSpinLimit) {
+                            fail();
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            copy_x(t);
+        }
+    } else {
+        // ---------------------------------------------------------- compute
+        // vector-memory instructions per ring refill
+        constexpr int kLoadsPerStage = FMT == Q4_INT4_ASYM ? 6 : 4;
+        (void)kLoadsPerStage;
+        const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * kChainCompute + wave);
+        const int total_waves = gridDim.x * kChainCompute;
+        // A wave's walk: task by task, its rows of the task and each row's
+        // stages.  Task t's rows are dealt to the waves from a rotated
+        // start, so that the waves holding one row more than the others
+        // differ from task to task.
+        auto first_pos = [&](int t) {
+            for (; t < nt; ++t) {
+                const int e =
+                    (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
+                if (e < a.t[t].N)
+                    return CPos{t, e, 0};
+            }
+            return CPos{nt, 0, 0};
+        };
+        auto advance = [&](CPos q) {
+            if (q.t >= nt)
+                return q;
+            if (++q.s == chain_stages(a.t[q.t].K)) {
+                q.s = 0;
+                q.row += total_waves;
+                if (q.row >= a.t[q.t].N)
+                    return first_pos(q.t + 1);
+            }
+            return q;
+        };
+        // Refills are issued unconditionally (past the last task from an
+        // empty view: the loads return zeros) so that the number of loads
+        // in flight is the same on every path and the waits stay partial.
+        auto load_pos = [&](Stage &st, CPos q) {
+            const bool live = q.t < nt;
+            const ChainTask &T = a.t[live ? q.t : nt - 1];
+            const RowViews v = row_views<FMT>(T.codes, T.scales, T.zeros, live ? q.row : T.N,
+                                              T.N, T.K >> 1, T.K >> a.gshift);
+            load_stage<FMT>(st, v, q.s, lane, a.gshift);
+        };
+        CPos pos[P];
+        Stage st[P];
+        pos[0] = first_pos(0);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            if (q > 0)
+                pos[q] = advance(pos[q - 1]);
+            st[q] = Stage{{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+            load_pos(st[q], pos[q]);
+        }
+        __syncthreads();  // the table, the counters and x of task 0
+        int cur = 0;
+        // Entering task cur + 1: count in, then wait for its x.  Before a
+        // task that reads earlier outputs, this wave's own stores complete
+        // first (the loader releases them to the grid).
+        auto enter = [&]() {
+            const int t = ++cur;
+            if (DEP && a.t[t].wait)
+                wait_vm<0>();
+            if (lane == 0)
+                __hip_atomic_fetch_add(&entered[t & 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            uint32_t spins = 0;
+            while (__hip_atomic_load(&ready[t & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != t) {
+                if (++spins == kSpinLimit) {
+                    fail();
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
+
+        // The ring: position q is computed while the next ones arrive, then
+        // its slot is refilled with the position P ahead.  A position of a
+        // later task first enters that task (and any task between without
+        // rows for this wave).  Each lane keeps its x slice (chunks l and
+        // 64 + l of the position's stage) in registers, read from LDS when
+        // the task or the stage changes.
+        //
+        // A round of the ring is never left in the middle (the load waits
+        // stay partial only if every path refills every slot): a position
+        // past the last task has loaded zeros from an empty view; it is
+        // computed on them and writes nothing.
+        u32x4 xreg[8];
+        float xinv_reg[2] = {1.0f, 1.0f};
+        int xkey = -1;
+        float acc[1] = {0.0f};
+        while (pos[0].t < nt) {
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const CPos cp = pos[q];
+                const bool live = cp.t < nt;
+                if (live) {
+                    while (cur < cp.t)
+                        enter();
+                }
+                const ChainTask &T = a.t[live ? cp.t : nt - 1];
+                const int S = chain_stages(T.K);
+                const int key = 8 * cp.t + cp.s;
+                if (key != xkey) {
+                    chain_x_slice(xreg, xinv_reg, lin[cp.t & 1], xinv_lds[cp.t & 1], cp.s, lane,
+                                  T.K >> 5);
+                    xkey = key;
+                }
+                const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
+                compute_stage<FMT, F::ct, F::pair, 1, X_REG>(st[q], acc, tbl, nullptr, xreg, xinv,
+                                                           make_rsrc(T.x, 0), T.K, S * kStageXBytes,
+                                                           cp.s, lane, T.K >> 5, laneoff);
+                if (cp.s == S - 1) {
+                    const float out = wave_sum(acc[0]);
+                    acc[0] = 0.0f;
+                    if (live && lane == 0)
+                        T.y[cp.row] = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                }
+                pos[q] = advance(pos[(q + P - 1) % P]);
+                load_pos(st[q], pos[q]);
+            }
+        }
+        // waves with no rows in the last tasks still count into them
+        while (cur < nt - 1)
+            enter();
+    }
+    wait_vm<0>();  // no LDS DMA may be in flight when the workgroup ends
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // the last workgroup to finish leaves the counters at zero for the
+        // next chain on this sync buffer (every workgroup is past its last
+        // barrier by then)
+        const uint32_t d =
+            __hip_atomic_fetch_add(&a.sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == gridDim.x - 1) {
+            __hip_atomic_store(&a.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sync[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Staged activations fit when M rows of whole stages, skewed, fit the region
+// (the last 16-byte piece ends at xpad(bytes - 16) + 16).
 bool x_fits_lds(int64_t M, int64_t K)
 {
     const int64_t C = K / 32;
     const int64_t S = (C + kStageChunks - 1) / kStageChunks;
     const int64_t bytes = M * S * kStageXBytes;
-    return bytes + (bytes >> 3) + 16 <= kXBytes;
+    return bytes - 16 + ((bytes - 16) >> 6 << 4) + 16 <= kXBytes;
 }
 
 template <int FMT, int ACT, int MT, int XS>
@@ -607,7 +1020,50 @@ hipError_t launch_act(q4_dtype act_t, const void *x, int M, const uint8_t *codes
     return launch_m<FMT, Q4_F16>(x, M, codes, scales, zeros, N, K, gshift, y, s);
 }
 
+template <int FMT, int ACT>
+hipError_t launch_chain_t(const ChainArgs &args, hipStream_t s)
+{
+    constexpr int depth = Q4_GEMV_CHAIN_DEPTH;
+    const int cus = device_cu_count();
+    if (cus <= 0)
+        return hipErrorInvalidDevice;
+    bool dep = false;
+    for (int i = 1; i < args.ntasks; ++i)
+        dep = dep || args.t[i].wait;
+    void *kargs[] = {const_cast<ChainArgs *>(&args)};
+    const void *fn = dep ? (const void *)gemv_chain_kernel<FMT, ACT, depth, true>
+                         : (const void *)gemv_chain_kernel<FMT, ACT, depth, false>;
+    return hipLaunchCooperativeKernel(fn, dim3(cus), dim3(1024), kargs, 0, s);
+}
+
 }  // namespace
+
+bool gemv_chain_k_ok(int64_t K) { return K <= kChainMaxK; }
+
+hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                             int ntasks, uint32_t *sync, hipStream_t s)
+{
+    ChainArgs a = {};
+    for (int i = 0; i < ntasks; ++i) {
+        a.t[i] = ChainTask{(const uint16_t *)tasks[i].x, tasks[i].codes, tasks[i].scales,
+                           tasks[i].zeros, (uint16_t *)tasks[i].y, (int)tasks[i].N,
+                           (int)tasks[i].K, (tasks[i].flags & Q4_TASK_NO_WAIT) ? 0 : 1};
+    }
+    a.ntasks = ntasks;
+    a.gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
+    a.sync = sync;
+    const bool bf = act_t == Q4_BF16;
+    switch (f) {
+    case Q4_NF4:
+        return bf ? launch_chain_t<Q4_NF4, Q4_BF16>(a, s) : launch_chain_t<Q4_NF4, Q4_F16>(a, s);
+    case Q4_INT4_SYM:
+        return bf ? launch_chain_t<Q4_INT4_SYM, Q4_BF16>(a, s)
+                  : launch_chain_t<Q4_INT4_SYM, Q4_F16>(a, s);
+    default:
+        return bf ? launch_chain_t<Q4_INT4_ASYM, Q4_BF16>(a, s)
+                  : launch_chain_t<Q4_INT4_ASYM, Q4_F16>(a, s);
+    }
+}
 
 hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                        const uint8_t *codes, const void *scales, const uint8_t *zeros, int64_t N,

@@ -158,6 +158,31 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                                     (hipStream_t)stream));
 }
 
+q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                        int ntasks, uint32_t *sync, void *stream)
+{
+    if (!format_ok(f) || !group_ok(g) || !dtype_ok(act_t))
+        return Q4_EUNSUPPORTED;
+    if (!tasks || !sync || ntasks <= 0)
+        return Q4_EINVAL;
+    if (ntasks > Q4_GEMV_CHAIN_MAX)
+        return Q4_EUNSUPPORTED;
+    if (!aligned(sync, 16))
+        return Q4_EALIGN;
+    for (int i = 0; i < ntasks; ++i) {
+        const q4_gemv_task &t = tasks[i];
+        q4_status st = check_product(f, g, act_t, t.x, 1, t.codes, t.scales, t.zeros, t.N, t.K,
+                                     t.y);
+        if (st != Q4_OK)
+            return st;
+        if ((t.flags & ~Q4_TASK_NO_WAIT) != 0)
+            return Q4_EINVAL;
+        if (t.K > Q4_GEMV_CHAIN_MAX_K || !q4::gemv_chain_k_ok(t.K))
+            return Q4_EUNSUPPORTED;
+    }
+    return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 int q4::device_cu_count()

@@ -30,8 +30,17 @@ SIGNATURES = {
     "q4_dequantize": (_int, [_int, _int, _vp, _vp, _vp, _i64, _i64, _int, _vp, _vp]),
     "q4_gemv": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "q4_gemm": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "q4_gemv_chain": (_int, [_int, _int, _int, ctypes.c_void_p, _int, _vp, _vp]),
     "q4_status_str": (ctypes.c_char_p, [_int]),
 }
+
+# q4_gemv_chain limits and the task record (layout of q4_gemv_task)
+CHAIN_MAX, CHAIN_MAX_K, CHAIN_SYNC_BYTES, TASK_NO_WAIT = 64, 16384, 16, 1
+
+
+class GemvTask(ctypes.Structure):
+    _fields_ = [("x", _vp), ("codes", _vp), ("scales", _vp), ("zeros", _vp), ("y", _vp),
+                ("N", _i64), ("K", _i64), ("flags", ctypes.c_uint32)]
 
 _lock = threading.Lock()
 _lib = None
@@ -189,3 +198,46 @@ def gemv(x, q: QuantizedWeight, out=None):
 def gemm(x, q: QuantizedWeight, out=None):
     """y = x . What^T for any M (q4_gemm, matrix cores)."""
     return _product("q4_gemm", x, q, out)
+
+
+def chain_sync(device):
+    """A zeroed sync buffer for gemv_chain (words 0-1 counters, word 2 the
+    timeout flag); reusable by later chains on the same stream."""
+    torch = _torch()
+    return torch.zeros((CHAIN_SYNC_BYTES // 4,), dtype=torch.int32, device=device)
+
+
+def gemv_chain(tasks, sync=None):
+    """Run M = 1 GEMVs in order in one launch (q4_gemv_chain).
+
+    tasks: sequence of (x [1, K], QuantizedWeight, y [1, N] or None[, flags]);
+    every weight shares one format and group size, every x one dtype.
+    Returns the list of outputs."""
+    torch = _torch()
+    if not tasks:
+        raise ValueError("empty chain")
+    q0 = tasks[0][1]
+    act = _act_code(tasks[0][0].dtype)
+    arr = (GemvTask * len(tasks))()
+    outs = []
+    for i, t in enumerate(tasks):
+        x, q, y = t[0], t[1], t[2]
+        flags = t[3] if len(t) > 3 else 0
+        _cuda(x, "x")
+        if (q.fmt, q.g) != (q0.fmt, q0.g) or _act_code(x.dtype) != act:
+            raise ValueError("chain tasks must share format, group size and activation dtype")
+        if x.dim() != 2 or x.shape != (1, q.K):
+            raise ValueError("x must be [1, K]")
+        if y is None:
+            y = torch.empty((1, q.N), dtype=x.dtype, device=x.device)
+        _cuda(y, "y")
+        arr[i] = GemvTask(_ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.zeros), _ptr(y),
+                          q.N, q.K, flags)
+        outs.append(y)
+    if sync is None:
+        sync = chain_sync(tasks[0][0].device)
+    _cuda(sync, "sync")
+    st = lib().q4_gemv_chain(q0.fmt, q0.g, act, ctypes.addressof(arr), len(tasks), _ptr(sync),
+                             _stream_ptr(tasks[0][0]))
+    _check(st, "q4_gemv_chain")
+    return outs

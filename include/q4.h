@@ -130,6 +130,44 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
                   int64_t N, int64_t K, void *y, void *stream);
 
+/* A chain of decode GEMVs in one launch.  Each task is one M = 1 product
+ * y[1, N] = x[1, K] . What^T with the layout and alignment rules of q4_gemv;
+ * all tasks share the format, group size and activation dtype.  The tasks run
+ * in order with the semantics of consecutive q4_gemv calls on the stream (and
+ * the same bits in y): unless its flags hold Q4_TASK_NO_WAIT, a task reads x
+ * only after every earlier task of the chain has written its y, so x may be
+ * an earlier task's output.  Weights are read ahead across task boundaries,
+ * so no task may write another task's weights.  Used for the weight stream of
+ * a decode step, whose GEMVs are otherwise dominated by per-launch cost when
+ * launched one by one ("Why it matters for deployment": a decode step reads
+ * every weight once).
+ *
+ * ntasks is 1..Q4_GEMV_CHAIN_MAX; each K must satisfy K <= Q4_GEMV_CHAIN_MAX_K
+ * (else Q4_EUNSUPPORTED); N and K are checked as in q4_gemv.  `sync` is a
+ * device buffer of Q4_GEMV_CHAIN_SYNC_BYTES, 16-byte aligned, zeroed by the
+ * caller before its first use: the kernel returns words 0 and 1 to zero when
+ * it ends, so the buffer can be reused without clearing by later chains on
+ * the same stream; chains that may overlap (other streams) need their own.
+ * Word 2 becomes nonzero if a wait between tasks gave up after about a second
+ * (the grid could not make progress; y is then undefined) and stays set until
+ * the caller clears it.  The chain is one cooperative launch of one
+ * workgroup per compute unit: a launch the runtime refuses returns Q4_EHIP. */
+#define Q4_GEMV_CHAIN_MAX 64
+#define Q4_GEMV_CHAIN_MAX_K 16384
+#define Q4_GEMV_CHAIN_SYNC_BYTES 16
+#define Q4_TASK_NO_WAIT 1u /* x is not written by earlier tasks: no grid-wide wait */
+typedef struct {
+    const void *x;        /* [1, K] act_t */
+    const uint8_t *codes; /* [N, K/2] */
+    const void *scales;   /* [N, K/g] */
+    const uint8_t *zeros; /* asym: packed zero-points; else NULL */
+    void *y;              /* [1, N] act_t */
+    int64_t N, K;
+    uint32_t flags;       /* 0 or Q4_TASK_NO_WAIT */
+} q4_gemv_task;
+q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                        int ntasks, uint32_t *sync, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *q4_status_str(q4_status s);
 

@@ -3,6 +3,7 @@ every symbol include/q4.h declares, reproduces the pages' byte arithmetic
 through its size helpers, and rejects bad arguments with the documented
 status codes before any HIP call."""
 
+import ctypes
 import json
 import os
 import re
@@ -145,3 +146,40 @@ def test_dequantize_rejects():
     assert L.q4_dequantize(q4.NF4, 64, A, A, None, 4, 128, q4.F16, None, None) == q4.EINVAL
     assert L.q4_dequantize(q4.NF4, 64, A, A, None, 4, 128, q4.F16, MIS, None) == q4.EALIGN
     assert L.q4_dequantize(q4.NF4, 64, A, MIS, None, 4, 128, q4.F16, A, None) == q4.EALIGN
+
+
+def call_chain(n=2, fmt=q4.NF4, g=64, act=q4.BF16, sync=A, **task_kw):
+    arr = (q4.GemvTask * max(n, 1))()
+    for i in range(max(n, 1)):
+        kw = dict(x=A, codes=A, scales=A, zeros=None, y=A, N=4, K=128, flags=0)
+        if i == n - 1:
+            kw.update(task_kw)
+        arr[i] = q4.GemvTask(**kw)
+    return q4.lib().q4_gemv_chain(fmt, g, act, ctypes.addressof(arr), n, sync, None)
+
+
+def test_gemv_task_layout():
+    # q4_gemv_task: five pointers, two int64 sizes, uint32 flags (+4 padding)
+    assert ctypes.sizeof(q4.GemvTask) == 64
+    assert q4.GemvTask.N.offset == 40 and q4.GemvTask.flags.offset == 56
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=3), q4.EUNSUPPORTED),
+    (dict(g=16), q4.EUNSUPPORTED),
+    (dict(act=2), q4.EUNSUPPORTED),
+    (dict(n=0), q4.EINVAL),
+    (dict(n=65), q4.EUNSUPPORTED),
+    (dict(sync=None), q4.EINVAL),
+    (dict(sync=0x10004), q4.EALIGN),
+    (dict(x=None), q4.EINVAL),
+    (dict(y=None), q4.EINVAL),
+    (dict(x=MIS), q4.EALIGN),
+    (dict(N=0), q4.EINVAL),
+    (dict(K=96), q4.EINVAL),
+    (dict(zeros=A), q4.EINVAL),
+    (dict(flags=2), q4.EINVAL),
+    (dict(K=16384 + 64), q4.EUNSUPPORTED),       # x no longer fits the LDS buffers
+])
+def test_chain_rejects(kw, status):
+    assert call_chain(**kw) == status
