@@ -138,7 +138,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// Buffer views of the weight arrays starting at row n0.
+// Buffer views of one weight row n0: its codes, scales and zero-point bytes
+// (empty for n0 >= N, so a position past the last row loads zeros).
 struct RowViews {
     __amdgpu_buffer_rsrc_t codes, scales, zeros;
     int zpar;  // parity of the row's first flat group index
@@ -150,13 +151,14 @@ __device__ __forceinline__ RowViews row_views(const uint8_t *codes, const void *
                                               int64_t row_bytes, int64_t G)
 {
     constexpr int ss = FMT == Q4_NF4 ? 4 : 2;
+    const bool live = n0 < N;
     RowViews v;
-    v.codes = make_rsrc(codes + n0 * row_bytes, (N - n0) * row_bytes);
-    v.scales = make_rsrc((const char *)scales + n0 * G * ss, (N - n0) * G * ss);
+    v.codes = make_rsrc(codes + n0 * row_bytes, live ? row_bytes : 0);
+    v.scales = make_rsrc((const char *)scales + n0 * G * ss, live ? G * ss : 0);
     const int64_t g0 = n0 * G;
     v.zpar = (int)(g0 & 1);
     if constexpr (FMT == Q4_INT4_ASYM)
-        v.zeros = make_rsrc(zeros + (g0 >> 1), (N * G + 1) / 2 - (g0 >> 1));
+        v.zeros = make_rsrc(zeros + (g0 >> 1), live ? ((g0 + G - 1) >> 1) - (g0 >> 1) + 1 : 0);
     else
         v.zeros = v.codes;
     return v;
@@ -179,23 +181,28 @@ __device__ __forceinline__ int stage_chunk(int s, int lane, int h) { return kSta
 // not kept in the caches (the "nt" cache-policy bit).
 constexpr int kNT = 2;
 
+// Chunks past the row end (C chunks per row) are sent out of the row's
+// views, so they read zeros without touching memory (their activations are
+// zero as well).
 template <int FMT>
-__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, int lane, int gshift)
+__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, int lane, int gshift,
+                                           int C)
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int ch = stage_chunk(s, lane, h);
-        // chunks past the row end read neighbouring (or out-of-range, hence
-        // zero) data; their activations are zero, so they add nothing
-        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, 16 * ch, 0, kNT);
+        const bool in = ch < C;
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, in ? 16 * ch : -16, 0, kNT);
         const int gl = (32 * ch) >> gshift;  // group index within the row
         if constexpr (FMT == Q4_NF4)
-            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(v.scales, 4 * gl, 0, kNT));
+            st.sc[h] = std::bit_cast<float>(
+                __builtin_amdgcn_raw_buffer_load_b32(v.scales, in ? 4 * gl : -16, 0, kNT));
         else
-            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, 2 * gl, 0, kNT));
+            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, in ? 2 * gl : -16, 0, kNT));
         if constexpr (FMT == Q4_INT4_ASYM) {
             const int gz = gl + v.zpar;
-            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, gz >> 1, 0, kNT);
+            const uint32_t b =
+                __builtin_amdgcn_raw_buffer_load_b8(v.zeros, in ? gz >> 1 : -16, 0, kNT);
             st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
         } else {
             st.zf[h] = 0.0f;
@@ -459,7 +466,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
         if (q > 0)
             pos[q] = advance(pos[q - 1]);
         const RowViews v = row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-        load_stage<FMT>(st[q], v, pos[q].s, lane, gshift);
+        load_stage<FMT>(st[q], v, pos[q].s, lane, gshift, C);
     }
 
     // fp16 conversion of bf16 activations with a power-of-two scale per
@@ -568,7 +575,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
             {
                 const RowViews v =
                     row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-                load_stage<FMT>(st[q], v, pos[q].s, lane, gshift);
+                load_stage<FMT>(st[q], v, pos[q].s, lane, gshift, C);
             }
             if (cp.s == S - 1) {
                 float out = 0.0f;
@@ -640,52 +647,76 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// A lane's x slice for stage s of a row: chunks l and 64 + l of the stage,
-// from LDS (zero past K), with the inverse scales of their conversion.
-__device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2], const char *lin,
-                                              const float *inv, int s, int lane, int C)
+#ifndef CHAIN_XB
+#define CHAIN_XB 2
+#endif
+
+// x of a chained task in LDS: piece-major within each stage (stage s, piece
+// j of its local chunk c at 16-byte index 512 s + 128 j + c), so that the 16
+// lanes of a read pass take 256 consecutive bytes (no bank conflicts).
+__device__ __forceinline__ int chain_x_index(int s, int j, int c) { return 512 * s + 128 * j + c; }
+
+// A lane's x slice for stage s of a row: chunks l and 64 + l of the stage
+// (the stored rows are zero past K up to whole stages), with the inverse
+// scales of their conversion.
+__device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2], const u32x4 *xb,
+                                              const float *inv, int s, int lane)
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int ch = stage_chunk(s, lane, h);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            xreg[4 * h + j] = ch < C ? *(const u32x4 *)(lin + 64 * ch + 16 * j) : u32x4{0, 0, 0, 0};
-        xinv[h] = ch < C ? inv[ch] : 1.0f;
+            xreg[4 * h + j] = xb[chain_x_index(s, j, 64 * h + lane)];
+        xinv[h] = inv[stage_chunk(s, lane, h)];
     }
 }
 
-// In-place conversion of x (linear, C chunks) where the arithmetic uses fp16
-// for bf16 activations: per 32-value chunk, max |x| scaled into
-// [2^14, 2^15) by a power of two (the staged single-product conversion);
-// inv receives the chunks' inverse scales (1 when nothing is converted).
+// The loader's copy of x[0, K) of a task into LDS, zero-padded to whole
+// stages, CHAIN_XB chunks of 32 values per lane at a time: converted where the arithmetic
+// uses fp16 for bf16 activations (per 32-value chunk, max |x| scaled into
+// [2^14, 2^15) by a power of two: the staged single-product conversion),
+// written piece-major; inv receives the chunks' inverse scales (1 when
+// nothing is converted).
 template <int FMT, int ACT>
-__device__ __forceinline__ void chain_convert_x(char *lin, float *inv, int C, int lane)
+__device__ __forceinline__ void chain_load_x(const ChainTask &T, u32x4 *xb, float *inv, int lane)
 {
     using F = Cfg<FMT, ACT, X_LDS>;
-    for (int ch = lane; ch < C; ch += 64) {
-        if constexpr (F::conv_x) {
-            u32x4 v[4];
-            float mx = 0.0f;
+    constexpr int kB = CHAIN_XB;  // chunks per lane per batch
+    // chunks up to the end of the last stage: past K the loads return zeros
+    const int C = chain_stages(T.K) * kStageChunks;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
+    for (int c0 = 0; c0 < C; c0 += 64 * kB) {
+        u32x4 v[kB][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[j] = *(const u32x4 *)(lin + 64 * ch + 16 * j);
+        for (int i = 0; i < kB; ++i)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    mx = fmaxf(mx, bf2_absmax(v[j][k]));
+            for (int j = 0; j < 4; ++j)
+                v[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, 64 * (c0 + 64 * i + lane) + 16 * j, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const int c = c0 + 64 * i + lane;
+            float iv = 1.0f;
+            if constexpr (F::conv_x) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        mx = fmaxf(mx, bf2_absmax(v[i][j][k]));
+                float f;
+                x_scale(mx, f, iv);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        v[i][j][k] = bf2_to_h2(v[i][j][k], f);
             }
-            float f, iv;
-            x_scale(mx, f, iv);
+            if (c < C) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    v[j][k] = bf2_to_h2(v[j][k], f);
-                *(u32x4 *)(lin + 64 * ch + 16 * j) = v[j];
+                for (int j = 0; j < 4; ++j)
+                    xb[chain_x_index(c >> 7, j, c & 127)] = v[i][j];
+                inv[c] = iv;
             }
-            inv[ch] = iv;
-        } else {
-            inv[ch] = 1.0f;
         }
     }
 }
@@ -705,14 +736,14 @@ void gemv_chain_kernel(const ChainArgs a)
     // address is the v_perm result itself.
     struct Lds {
         uint32_t tbl[kTableDwords];
-        char lin[2][kChainLinBytes];
+        u32x4 xb[2][kChainLinBytes / 16];
         float xinv[2][kChainMaxK / 32];
         int entered[2];  // compute waves that entered tasks of each parity (cumulative)
         int ready[2];    // the task whose x lin[parity] holds
     };
     __shared__ Lds lds;
     uint32_t *const tbl = lds.tbl;
-    auto &lin = lds.lin;
+    auto &xb = lds.xb;
     auto &xinv_lds = lds.xinv;
     auto &entered = lds.entered;
     auto &ready = lds.ready;
@@ -764,17 +795,8 @@ void gemv_chain_kernel(const ChainArgs a)
     if (wave == kChainCompute) {
         // ---------------------------------------------------------- loader
         auto copy_x = [&](int t) {
-            const ChainTask &T = a.t[t];
-            const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
-            const int n1k = (2 * T.K + 1023) >> 10;
-            char *dst = lin[t & 1];
-            for (int b = 0; b < n1k; ++b)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    xr, (__attribute__((address_space(3))) void *)(dst + 1024 * b), 16, 16 * lane,
-                    1024 * b, 0, 0);
-            wait_vm<0>();
-            chain_convert_x<FMT, ACT>(dst, xinv_lds[t & 1], T.K >> 5, lane);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the converted x is in LDS
+            chain_load_x<FMT, ACT>(a.t[t], xb[t & 1], xinv_lds[t & 1], lane);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): x is in LDS
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __hip_atomic_store(&ready[t & 1], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
@@ -861,7 +883,7 @@ void gemv_chain_kernel(const ChainArgs a)
             const ChainTask &T = a.t[live ? q.t : nt - 1];
             const RowViews v = row_views<FMT>(T.codes, T.scales, T.zeros, live ? q.row : T.N,
                                               T.N, T.K >> 1, T.K >> a.gshift);
-            load_stage<FMT>(st, v, q.s, lane, a.gshift);
+            load_stage<FMT>(st, v, q.s, lane, a.gshift, T.K >> 5);
         };
         CPos pos[P];
         Stage st[P];
@@ -923,8 +945,7 @@ void gemv_chain_kernel(const ChainArgs a)
                 const int S = chain_stages(T.K);
                 const int key = 8 * cp.t + cp.s;
                 if (key != xkey) {
-                    chain_x_slice(xreg, xinv_reg, lin[cp.t & 1], xinv_lds[cp.t & 1], cp.s, lane,
-                                  T.K >> 5);
+                    chain_x_slice(xreg, xinv_reg, xb[cp.t & 1], xinv_lds[cp.t & 1], cp.s, lane);
                     xkey = key;
                 }
                 const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
