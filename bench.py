@@ -22,6 +22,9 @@ The same run also measures, each with HIP events on the launch stream:
   * dequantize of a 14336x4096 INT4-asym weight to bf16,
   * the prefill GEMM M=2048, N=14336, K=4096, INT4-asym g32, bf16 x
     (TFLOP/s against the dense bf16 matrix-core peak),
+  * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
+    INT4-sym g128 4096x4096 at M = 1, NF4 g64 11008x4096 and 4096x11008 at
+    M = 1, 4, 16,
   * the CPU oracle on a time-bounded sample of the token (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -253,6 +256,7 @@ def main():
     extra = {}
     if not args.skip_extra:
         extra = extra_legs(torch, q4, dev, stream)
+        extra["gemv_configs_cold"] = config_gemvs(torch, q4, dev, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -363,6 +367,83 @@ def one_leg(leg, torch, q4, dev, stream):
     ms = timed(lambda: q4.gemm(x, q, out=y), 5)
     return {"leg": "gemm", "ms": round(ms, 4),
             "TFLOPs": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+
+
+def _rotated_gemv(torch, q4, dev, stream, fmt, g, N, K, Ms, act, seed, min_bytes=512 << 20):
+    """GEMV weight GB/s on cold weights: R copies of one quantized matrix
+    (R * bytes >= 512 MiB, more than the 256 MB last-level cache), used in
+    turn, timed per launch with HIP events (median and minimum), and the
+    same R launches back to back from a HIP graph (per-launch average)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w = torch.empty((N, K), dtype=torch.float16, device=dev).normal_(0.0, 0.02, generator=gen)
+    q0 = q4.quantize(w, fmt, g)
+    nb = q0.nbytes()
+    R = max(2, -(-min_bytes // nb))
+    qs = [q0] + [q4.quantize(w, fmt, g) for _ in range(R - 1)]
+    del w
+    dt = torch.bfloat16 if act == q4.BF16 else torch.float16
+    out = {}
+    for M in Ms:
+        x = torch.randn((M, K), generator=gen, device=dev).to(dt)
+        y = torch.empty((M, N), dtype=dt, device=dev)
+        for q in qs[:2]:
+            q4.gemv(x, q, out=y)
+        torch.cuda.synchronize()
+        reps = 3 * R
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            q4.gemv(x, qs[i % R], out=y)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        med = us[len(us) // 2]
+        # the same launches back to back, replayed from a HIP graph
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for q in qs:
+                q4.gemv(x, q, out=y)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for q in qs:
+                q4.gemv(x, q, out=y)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(3):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        g_us = a.elapsed_time(b) * 1e3 / (3 * R)
+        del graph
+        out[f"M{M}"] = {"us_median": round(med, 2), "us_min": round(us[0], 2),
+                        "weight_GBps": round(nb / (med * 1e-6) / 1e9, 1),
+                        "pct_hbm_peak": round(100 * nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                        "graph_us_per_launch": round(g_us, 2),
+                        "graph_weight_GBps": round(nb / (g_us * 1e-6) / 1e9, 1)}
+    del qs
+    torch.cuda.empty_cache()
+    return {"weight_bytes": nb, "copies": R, **out}
+
+
+def config_gemvs(torch, q4, dev, stream):
+    """The single-matrix GEMV configurations on cold weights: INT4-sym g128
+    4096x4096 (fp16 x, M = 1) and the NF4 g64 MLP shapes 11008x4096 and
+    4096x11008 (bf16 x, M = 1, 4, 16)."""
+    return {
+        "c2_sym_g128_4096x4096_f16": _rotated_gemv(torch, q4, dev, stream, q4.INT4_SYM, 128,
+                                                   4096, 4096, [1], q4.F16, 203),
+        "c3_nf4_g64_11008x4096_bf16": _rotated_gemv(torch, q4, dev, stream, q4.NF4, 64,
+                                                    11008, 4096, [1, 4, 16], q4.BF16, 303),
+        "c3_nf4_g64_4096x11008_bf16": _rotated_gemv(torch, q4, dev, stream, q4.NF4, 64,
+                                                    4096, 11008, [1, 4, 16], q4.BF16, 304),
+    }
 
 
 def extra_legs(torch, q4, dev, stream):

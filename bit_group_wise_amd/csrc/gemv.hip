@@ -1,5 +1,7 @@
 // gemv.hip -- decode-shape fused dequant-GEMV, y[M, N] = x[M, K] . What^T,
-// 1 <= M <= 16, with no matrix-core instructions.
+// M = 1 or 2, with no matrix-core instructions (three or more rows run as
+// the skinny matrix-core product of gemv_mfma.hip), and the chained M = 1
+// kernel behind q4_gemv_chain.
 //
 // Method ("Loading a model in 4-bit", "Where the accuracy goes"; "INT4
 // Quantization > Practical Implementation with bitsandbytes"): the layer
@@ -1013,7 +1015,7 @@ hipError_t launch_m(const void *x, int M, const uint8_t *codes, const void *scal
                     const uint8_t *zeros, int64_t N, int64_t K, int gshift, void *y, hipStream_t s)
 {
     // M = 1 with one stage per row: activations live in registers; else
-    // (M <= 2) staged in LDS when they fit; else read from L2
+    // staged in LDS when they fit; else read from L2 (M <= 2 here)
     const bool one_stage = K <= 32 * kStageChunks;
     const bool xl = x_fits_lds(M <= 1 ? 1 : 2, K);
 #define Q4_GEMV_LAUNCH(MT_, XS_) \
@@ -1021,13 +1023,7 @@ hipError_t launch_m(const void *x, int M, const uint8_t *codes, const void *scal
     if (M <= 1)
         return one_stage ? Q4_GEMV_LAUNCH(1, X_REG)
                          : (xl ? Q4_GEMV_LAUNCH(1, X_LDS) : Q4_GEMV_LAUNCH(1, X_GLOBAL));
-    if (M <= 2)
-        return xl ? Q4_GEMV_LAUNCH(2, X_LDS) : Q4_GEMV_LAUNCH(2, X_GLOBAL);
-    if (M <= 4)
-        return Q4_GEMV_LAUNCH(4, X_GLOBAL);
-    if (M <= 8)
-        return Q4_GEMV_LAUNCH(8, X_GLOBAL);
-    return Q4_GEMV_LAUNCH(16, X_GLOBAL);
+    return xl ? Q4_GEMV_LAUNCH(2, X_LDS) : Q4_GEMV_LAUNCH(2, X_GLOBAL);
 #undef Q4_GEMV_LAUNCH
 }
 
@@ -1090,6 +1086,9 @@ hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_
                        const uint8_t *codes, const void *scales, const uint8_t *zeros, int64_t N,
                        int64_t K, void *y, hipStream_t s)
 {
+    // three or more activation rows: the skinny matrix-core product
+    if (M >= 3)
+        return launch_gemv_mfma(f, g, act_t, x, M, codes, scales, zeros, N, K, y, s);
     const int gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
     switch (f) {
     case Q4_NF4:

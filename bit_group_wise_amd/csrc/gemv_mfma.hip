@@ -1,0 +1,215 @@
+// gemv_mfma.hip -- skinny product y[M, N] = x[M, K] . What^T for M <= 16 on
+// the matrix cores.
+//
+// Method ("Loading a model in 4-bit", "Where the accuracy goes"; "INT4
+// Quantization > Practical Implementation with bitsandbytes"): the weights
+// are dequantized to the 16-bit compute dtype (each value as q4_dequantize
+// writes it) and multiplied with fp32 accumulation.  With a few activation
+// rows the product still streams every weight byte once ("What is 4-bit
+// quantization and why does it matter?", "Why it matters for deployment"),
+// but the per-weight work grows with M, so from 3 rows on it runs here on
+// v_mfma_f32_16x16x32 instead of the vector ALUs.
+//
+// gfx950 mapping:
+//  * A workgroup owns 16 weight rows (one MFMA operand of 16 rows) and all
+//    M <= 16 activation rows; its 8 waves split K into steps of 128,
+//    interleaved (wave w takes steps w, w + 8, ...), so even a 4096-row
+//    matrix gives 2048 streaming waves.
+//  * Lane (r, q) = (lane % 16, lane / 16) loads 16 bytes of codes: 32
+//    weights of row r at k = k0 + 32 q.  Dword d of them is the lane's share
+//    of MFMA d of the step, which therefore contracts over k0 + 32 q + 8 d
+//    ... + 7 for lane quad q; the activation operand uses the same order, so
+//    lane (m, q) loads x[m][k0 + 32 q ... + 31] as four 16-byte pieces.
+//    Every load is contiguous; x rows past M and k past K are sent out of
+//    range and read zeros.
+//  * A 2-deep ring of steps keeps the next step's loads in flight.
+//  * The 8 partial 16 x 16 tiles meet in LDS and are summed in wave order
+//    (a fixed order, so the result does not depend on timing).
+#include "q4_common.hpp"
+#include "q4_internal.hpp"
+#include "q4_mfma.hpp"
+
+namespace q4 {
+namespace {
+
+constexpr int kSkWaves = 8;
+constexpr int kSkBlock = 64 * kSkWaves;
+constexpr int kSkStep = 128;  // k per step
+#ifndef Q4_SK_RING
+#define Q4_SK_RING 2
+#endif
+constexpr int kSkRing = Q4_SK_RING;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void *base, int64_t bytes)
+{
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+
+// One step's operands for a lane: 32 codes, their group's scale (and asym
+// zero-point), and 32 activations of one x row.
+template <int FMT>
+struct SkStep {
+    u32x4 cw;
+    uint32_t sraw;
+    uint32_t zraw;
+    u32x4 xv[4];
+};
+
+template <int FMT, int ACT>
+__global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K, int gshift,
+    uint16_t *__restrict__ y)
+{
+    __shared__ float2 ptbl[FMT == Q4_NF4 ? 256 : 1];
+    __shared__ f32x4 part[kSkWaves][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int G = K >> gshift;
+    const int row_bytes = K >> 1;
+    constexpr int ss = FMT == Q4_NF4 ? 4 : 2;
+
+    if constexpr (FMT == Q4_NF4) {
+        if (threadIdx.x < 256)
+            ptbl[threadIdx.x] = float2{kNF4[threadIdx.x & 15], kNF4[threadIdx.x >> 4]};
+    }
+
+    // views: this block's 16 weight rows (rows past N read zeros) and the M
+    // activation rows
+    const int nrows = N - n0 < 16 ? N - n0 : 16;
+    const __amdgpu_buffer_rsrc_t cr = sk_rsrc(codes + (int64_t)n0 * row_bytes, (int64_t)nrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t sr =
+        sk_rsrc((const char *)scales + (int64_t)n0 * G * ss, (int64_t)nrows * G * ss);
+    const int64_t zg0 = (int64_t)n0 * G;  // flat group index of the block's first group
+    __amdgpu_buffer_rsrc_t zr = sr;
+    if constexpr (FMT == Q4_INT4_ASYM)
+        zr = sk_rsrc(zeros + (zg0 >> 1), (((int64_t)nrows * G + (zg0 & 1)) + 1) / 2);
+    const __amdgpu_buffer_rsrc_t xr = sk_rsrc(x, (int64_t)M * K * 2);
+
+    const int nsteps = (K + kSkStep - 1) / kSkStep;
+    auto load = [&](SkStep<FMT> &st, int step) {
+        const int k = step * kSkStep + 32 * q;  // the lane's first k
+        const bool in = step < nsteps && k < K;
+        st.cw = __builtin_amdgcn_raw_buffer_load_b128(cr, in ? r * row_bytes + (k >> 1) : -16, 0, 0);
+        const int gi = r * G + (k >> gshift);  // group within the block
+        if constexpr (FMT == Q4_NF4)
+            st.sraw = __builtin_amdgcn_raw_buffer_load_b32(sr, in ? 4 * gi : -16, 0, 0);
+        else
+            st.sraw = __builtin_amdgcn_raw_buffer_load_b16(sr, in ? 2 * gi : -16, 0, 0);
+        if constexpr (FMT == Q4_INT4_ASYM) {
+            const int gz = (int)(zg0 & 1) + gi;
+            st.zraw = __builtin_amdgcn_raw_buffer_load_b8(zr, in ? gz >> 1 : -16, 0, 0) >>
+                      (4 * (gz & 1));
+        } else {
+            st.zraw = 0;
+        }
+        const bool xin = in && r < M;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            st.xv[d] = __builtin_amdgcn_raw_buffer_load_b128(
+                xr, xin ? 2 * (r * K + k + 8 * d) : -16, 0, 0);
+    };
+
+    // the wave's steps: wave, wave + 8, ...
+    SkStep<FMT> ring[kSkRing];
+#pragma unroll
+    for (int i = 0; i < kSkRing; ++i)
+        load(ring[i], wave + kSkWaves * i);
+    __syncthreads();  // the level-pair table
+
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int step = wave; step < nsteps; step += kSkWaves * kSkRing) {
+#pragma unroll
+        for (int i = 0; i < kSkRing; ++i) {
+            const int cs = step + kSkWaves * i;
+            SkStep<FMT> &st = ring[i];
+            // every path computes (a step past the end has zero codes,
+            // scales and x), so the load waits stay partial
+            float s, b;
+            if constexpr (FMT == Q4_NF4) {
+                s = std::bit_cast<float>(st.sraw);
+                b = 0.0f;
+            } else {
+                s = h2f(st.sraw & 0xffffu);
+                b = FMT == Q4_INT4_SYM ? -8.0f * s : -(float)(st.zraw & 0xfu) * s;
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float2 lp[4];
+                if constexpr (FMT == Q4_NF4) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lp[e] = ptbl[(st.cw[d] >> (8 * e)) & 0xffu];
+                }
+                const u32x4 wf = dequant8<FMT, ACT>(st.cw[d], s, b, lp);
+                acc = mfma<ACT>(wf, st.xv[d], acc);
+            }
+            (void)cs;
+            load(st, step + kSkWaves * (i + kSkRing));
+        }
+    }
+
+    // sum the 8 partial tiles in wave order; lane l holds rows 4 q + v of
+    // the block against activation row r
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 t = part[0][lane];
+#pragma unroll
+        for (int w = 1; w < kSkWaves; ++w) {
+            const f32x4 u = part[w][lane];
+            t = f32x4{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
+        }
+        const int m = r;
+        const int n = n0 + 4 * q;
+        if (m < M) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (n + v < N)
+                    y[(int64_t)m * N + n + v] =
+                        (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(t[v]) : f2h_bits(t[v]));
+            }
+        }
+    }
+}
+
+template <int FMT>
+hipError_t launch_sk_fmt(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
+                         const void *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                         int gshift, void *y, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    if (act_t == Q4_BF16)
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_BF16>), dim3(blocks), dim3(kSkBlock), 0, s,
+                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
+                           (uint16_t *)y);
+    else
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_F16>), dim3(blocks), dim3(kSkBlock), 0, s,
+                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
+                           (uint16_t *)y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                            const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                            int64_t N, int64_t K, void *y, hipStream_t s)
+{
+    const int gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
+    switch (f) {
+    case Q4_NF4:
+        return launch_sk_fmt<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    case Q4_INT4_SYM:
+        return launch_sk_fmt<Q4_INT4_SYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    default:
+        return launch_sk_fmt<Q4_INT4_ASYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    }
+}
+
+}  // namespace q4

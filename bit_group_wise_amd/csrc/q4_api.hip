@@ -154,6 +154,11 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
         return st;
     if (K > Q4_GEMM_MAX_K)
         return Q4_EUNSUPPORTED;
+    // up to 16 activation rows: the skinny product (a 256-row tile would be
+    // mostly empty)
+    if (M <= 16)
+        return from_hip(q4::launch_gemv_mfma(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
+                                             (hipStream_t)stream));
     return from_hip(q4::launch_gemm(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                     (hipStream_t)stream));
 }

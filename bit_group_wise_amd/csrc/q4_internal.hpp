@@ -29,6 +29,10 @@ hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const voi
 hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                        const uint8_t *codes, const void *scales, const uint8_t *zeros,
                        int64_t N, int64_t K, void *y, hipStream_t s);
+// Skinny product (M <= 16) on the matrix cores.
+hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                            const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                            int64_t N, int64_t K, void *y, hipStream_t s);
 // Chained M = 1 GEMVs (at most Q4_GEMV_CHAIN_MAX tasks per launch).
 bool gemv_chain_k_ok(int64_t K);
 hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,

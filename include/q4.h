@@ -115,6 +115,8 @@ q4_status q4_dequantize(q4_format f, int g, const uint8_t *codes, const void *sc
  * the packed weights once and dequantizing them in registers; fp32
  * accumulation, one rounding of y to act_t.  Equal to a 16-bit matmul on the
  * dequantized weights up to rounding order ("Where the accuracy goes").
+ * M = 1, 2 run on the vector ALUs; 3 <= M <= 16 as a skinny matrix-core
+ * product (weights dequantized to act_t as q4_dequantize writes them).
  * M > 16 returns Q4_EUNSUPPORTED (use q4_gemm). */
 q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
@@ -124,6 +126,7 @@ q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
  * tiles are dequantized to the activation dtype on the fly (each value as
  * q4_dequantize writes it) and multiplied on the matrix cores with fp32
  * accumulation; y is rounded once to act_t ("Where the accuracy goes").
+ * M <= 16 runs as the skinny product q4_gemv uses for 3 <= M <= 16.
  * K > Q4_GEMM_MAX_K returns Q4_EUNSUPPORTED. */
 #define Q4_GEMM_MAX_K 4194304
 q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
