@@ -22,6 +22,9 @@ The same run also measures, each with HIP events on the launch stream:
   * dequantize of a 14336x4096 INT4-asym weight to bf16,
   * the prefill GEMM M=2048, N=14336, K=4096, INT4-asym g32, bf16 x
     (TFLOP/s against the dense bf16 matrix-core peak),
+  * the unfused path (dequantize to bf16, then torch.matmul / hipBLASLt) at
+    the prefill shape and at M = 16 on an 11008x4096 NF4 weight, beside the
+    fused kernels,
   * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
     INT4-sym g128 4096x4096 at M = 1, NF4 g64 11008x4096 and 4096x11008 at
     M = 1, 4, 16,
@@ -460,10 +463,39 @@ def extra_legs(torch, q4, dev, stream):
     gt = timed(lambda: q4.gemm(x, q, out=y), 10)
     flops = 2.0 * M * N * K
     codec_bytes = N * K * 2 + q.nbytes()
+    # the pages' unfused path: dequantize to the compute dtype, then a
+    # library 16-bit GEMM (hipBLASLt through torch.matmul)
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def unfused():
+        q4.dequantize(q, torch.bfloat16, out=out)
+        torch.matmul(x, out.t(), out=yb)
+    ut = timed(unfused, 10)
+    mt = timed(lambda: torch.matmul(x, out.t(), out=yb), 10)
+    # the same at decode width: M = 16 on the c3 gate/up shape (NF4 g64)
+    w16 = torch.empty((11008, 4096), dtype=torch.float16, device=dev).normal_(0.0, 0.02)
+    q16 = q4.quantize(w16, q4.NF4, 64)
+    x16 = torch.randn((16, 4096), device=dev).to(torch.bfloat16)
+    o16 = torch.empty((11008, 4096), dtype=torch.bfloat16, device=dev)
+    y16 = torch.empty((16, 11008), dtype=torch.bfloat16, device=dev)
+
+    def unfused16():
+        q4.dequantize(q16, torch.bfloat16, out=o16)
+        torch.matmul(x16, o16.t(), out=y16)
+    u16 = timed(unfused16, 20)
+    f16t = timed(lambda: q4.gemv(x16, q16, out=y16), 20)
     return {
         "gemm": {"shape": f"M={M} N={N} K={K} int4_asym g32 bf16", "ms": round(gt, 4),
                  "TFLOPs": round(flops / (gt * 1e-3) / 1e12, 1),
                  "pct_bf16_peak": round(100 * flops / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)},
+        "unfused_dequant_then_hipblaslt": {
+            "prefill_M2048_ms": round(ut, 4),
+            "prefill_matmul_only_ms": round(mt, 4),
+            "prefill_matmul_only_TFLOPs": round(flops / (mt * 1e-3) / 1e12, 1),
+            "fused_over_unfused_prefill": round(ut / gt, 3),
+            "decode_M16_nf4_11008x4096_unfused_ms": round(u16, 4),
+            "decode_M16_nf4_11008x4096_fused_ms": round(f16t, 4),
+            "fused_over_unfused_M16": round(u16 / f16t, 3)},
         "dequantize_14336x4096_asym_bf16": {"ms": round(dt, 4),
                                              "GBps": round(codec_bytes / (dt * 1e-3) / 1e9, 1)},
         "quantize_14336x4096_asym": {"ms": round(qt, 4),
