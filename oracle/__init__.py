@@ -21,6 +21,11 @@ pages on 4-bit group-wise quantization):
   contiguous blocks, absmax per block, nearest of 16 entries after dividing by
   the absmax, dequantize = absmax times table value; "Where the accuracy goes":
   the product is an ordinary 16-bit matmul on dequantized weights.
+* Double quantization of the NF4 block constants ("Loading a model in 4-bit",
+  the double-quantization flag and "Where the accuracy goes"; the closing
+  section on NF4: blocks of 256 constants to 8 bits, 0.5 -> about 0.127 bits
+  per parameter).  Read as symmetric absmax int8 coding of each run of 256
+  absmax values (flat group order) with a binary32 constant per run.
 """
 
 from __future__ import annotations
@@ -32,9 +37,10 @@ import threading
 
 import numpy as np
 
-NF4, INT4_SYM, INT4_ASYM = 0, 1, 2
+NF4, INT4_SYM, INT4_ASYM, NF4_DQ = 0, 1, 2, 3
 F16, BF16 = 0, 1
-FORMAT_NAMES = {NF4: "nf4", INT4_SYM: "int4_sym", INT4_ASYM: "int4_asym"}
+FORMAT_NAMES = {NF4: "nf4", INT4_SYM: "int4_sym", INT4_ASYM: "int4_asym", NF4_DQ: "nf4_dq"}
+DQ_BLOCK = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q4_oracle.c")
@@ -77,6 +83,10 @@ def lib() -> ctypes.CDLL:
                                      _i64, _i64, _i64p, _i64, _f64p, _f64p]
             for f in (L.orc_quantize, L.orc_dequantize, L.orc_matmul):
                 f.restype = _int
+            L.orc_double_quant.argtypes = [_f32p, _i64, _u8p, _f32p]
+            L.orc_double_quant.restype = None
+            L.orc_dq_s2_offset.argtypes = [_i64]
+            L.orc_dq_s2_offset.restype = _i64
             L.orc_nf4_nearest.argtypes = [ctypes.c_float]
             L.orc_nf4_nearest.restype = _int
             L.orc_f32_to_f16_array.argtypes = [_f32p, _u16p, _i64]
@@ -133,11 +143,42 @@ def nf4_nearest(x) -> np.ndarray:
     return out
 
 
+def dq_s2_offset(n_groups: int) -> int:
+    """Byte offset of the second-level constants in an NF4_DQ scales buffer."""
+    return int(lib().orc_dq_s2_offset(n_groups))
+
+
+def dq_scales_size(n_groups: int) -> int:
+    """Bytes of an NF4_DQ scales buffer: codes (padded to 16) then s2."""
+    return dq_s2_offset(n_groups) + 4 * ((n_groups + DQ_BLOCK - 1) // DQ_BLOCK)
+
+
+def dq_split(scales, n_groups: int):
+    """(qc uint8[n_groups], s2 float32[ceil(n_groups/256)]) of an NF4_DQ
+    scales buffer (flat uint8)."""
+    b = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1)
+    off = dq_s2_offset(n_groups)
+    nb = (n_groups + DQ_BLOCK - 1) // DQ_BLOCK
+    return b[:n_groups].copy(), b[off:off + 4 * nb].copy().view(np.float32)
+
+
+def double_quant(c):
+    """Second-level quantization of an absmax array (flat order):
+    (qc uint8[n], s2 float32[ceil(n/256)])."""
+    c = np.ascontiguousarray(c, dtype=np.float32).reshape(-1)
+    n = c.size
+    qc = np.zeros(n, dtype=np.uint8)
+    s2 = np.zeros((n + DQ_BLOCK - 1) // DQ_BLOCK, dtype=np.float32)
+    lib().orc_double_quant(_p(c, _f32p), n, _p(qc, _u8p), _p(s2, _f32p))
+    return qc, s2
+
+
 def quantize(fmt: int, g: int, w_bits: np.ndarray):
     """Quantize fp16 weights given as uint16 bit patterns [N, K].
 
     Returns (codes uint8[N, K/2], scales, zeros) where scales is float32[N, K/g]
-    for NF4 and uint16 fp16 bits [N, K/g] for INT4, and zeros is uint8
+    for NF4, uint16 fp16 bits [N, K/g] for INT4 and, for NF4_DQ, the flat
+    uint8 buffer of dq_scales_size(N*K/g) bytes (see dq_split); zeros is uint8
     [ceil(N*K/g/2)] for INT4-asym, else None."""
     _check_g(g)
     w = np.ascontiguousarray(w_bits, dtype=np.uint16)
@@ -146,7 +187,10 @@ def quantize(fmt: int, g: int, w_bits: np.ndarray):
         raise ValueError("K must be a multiple of g")
     G = K // g
     codes = np.zeros((N, K // 2), dtype=np.uint8)
-    scales = np.zeros((N, G), dtype=np.float32 if fmt == NF4 else np.uint16)
+    if fmt == NF4_DQ:
+        scales = np.zeros(dq_scales_size(N * G), dtype=np.uint8)
+    else:
+        scales = np.zeros((N, G), dtype=np.float32 if fmt == NF4 else np.uint16)
     zeros = np.zeros(((N * G + 1) // 2,), dtype=np.uint8) if fmt == INT4_ASYM else None
     rc = lib().orc_quantize(fmt, g, _p(w, _u16p), N, K, _p(codes, _u8p),
                             scales.ctypes.data_as(_vp),

@@ -128,7 +128,7 @@ static int clampi(int v, int lo, int hi)
 
 static int valid_shape(int fmt, int g, int64_t N, int64_t K)
 {
-    if (fmt < ORC_NF4 || fmt > ORC_INT4_ASYM)
+    if (fmt < ORC_NF4 || fmt > ORC_NF4_DQ)
         return 0;
     if (g != 32 && g != 64 && g != 128)
         return 0;
@@ -157,7 +157,7 @@ static void quantize_group(int fmt, int g, const uint16_t *wg, int64_t gi,
                            int64_t e0, uint8_t *codes, void *scales,
                            uint8_t *zeros)
 {
-    if (fmt == ORC_NF4) {
+    if (fmt == ORC_NF4 || fmt == ORC_NF4_DQ) {
         /* [hf4]: c = max|w| over the block, stored as binary32 (an fp16 value
          * widened, so exact); code = nearest Q[i] to w / c. */
         float c = 0.0f;
@@ -224,6 +224,35 @@ static void quantize_group(int fmt, int g, const uint16_t *wg, int64_t gi,
     }
 }
 
+/* [dq] The block constants quantized again: consecutive runs of
+ * ORC_DQ_BLOCK absmax values (flat group order; the last run may be short)
+ * share one binary32 constant s2 = c2 / 127 with c2 the run's largest
+ * absmax, and each absmax becomes the 8-bit code q = rint(c / s2) clamped to
+ * 0..127 (symmetric absmax 8-bit coding; the absmax values are >= 0, so only
+ * the non-negative half of the levels occurs).  s2 == 0 (an all-zero run)
+ * gives q = 0. */
+void orc_double_quant(const float *c, int64_t n, uint8_t *qc, float *s2)
+{
+    for (int64_t b = 0; b * ORC_DQ_BLOCK < n; ++b) {
+        int64_t i0 = b * ORC_DQ_BLOCK;
+        int64_t i1 = i0 + ORC_DQ_BLOCK < n ? i0 + ORC_DQ_BLOCK : n;
+        float c2 = 0.0f;
+        for (int64_t i = i0; i < i1; ++i)
+            if (c[i] > c2)
+                c2 = c[i];
+        float s = c2 / 127.0f;                      /* binary32 division */
+        s2[b] = s;
+        for (int64_t i = i0; i < i1; ++i) {
+            int q = 0;
+            if (s != 0.0f)
+                q = clampi((int)rintf(c[i] / s), 0, 127);
+            qc[i] = (uint8_t)q;
+        }
+    }
+}
+
+int64_t orc_dq_s2_offset(int64_t n_groups) { return (n_groups + 15) / 16 * 16; }
+
 int orc_quantize(int fmt, int g, const uint16_t *w, int64_t N, int64_t K,
                  uint8_t *codes, void *scales, uint8_t *zeros)
 {
@@ -234,22 +263,55 @@ int orc_quantize(int fmt, int g, const uint16_t *w, int64_t N, int64_t K,
     int64_t G = K / g;
     if (zeros) /* a half-filled last byte keeps a zero high nibble */
         memset(zeros, 0, (size_t)((N * G + 1) / 2));
+    /* NF4_DQ: the codes are those of NF4 (made with the exact absmax); the
+     * absmax array is kept aside and then quantized as a whole */
+    void *first = scales;
+    float *c = NULL;
+    if (fmt == ORC_NF4_DQ) {
+        c = (float *)malloc((size_t)(N * G) * sizeof(float));
+        if (!c)
+            return -1;
+        first = c;
+    }
     for (int64_t r = 0; r < N; ++r)
         for (int64_t j = 0; j < G; ++j)
             quantize_group(fmt, g, w + r * K + j * g, r * G + j, r * K + j * g,
-                           codes, scales, zeros);
+                           codes, first, zeros);
+    if (c) {
+        int64_t nb = (N * G + ORC_DQ_BLOCK - 1) / ORC_DQ_BLOCK;
+        float *s2 = (float *)malloc((size_t)nb * sizeof(float));
+        if (!s2) {
+            free(c);
+            return -1;
+        }
+        uint8_t *out = (uint8_t *)scales;
+        int64_t off = orc_dq_s2_offset(N * G);
+        memset(out, 0, (size_t)off);
+        orc_double_quant(c, N * G, out, s2);
+        memcpy(out + off, s2, (size_t)nb * sizeof(float));
+        free(s2);
+        free(c);
+    }
     return 0;
 }
 
 /* [n4n] dequantize: value = table entry (or integer level) times the block
  * scale, one binary32 product, then one round-to-nearest-even to the output
  * dtype.  Sym: (nib - 8) * s; asym: (q - z) * s ([n4n] affine form with
- * zp = -z*s); NF4: Q[i] * c ([hf4]). */
-static float dequant_value(int fmt, int nib, int64_t gi, const void *scales,
-                           const uint8_t *zeros)
+ * zp = -z*s); NF4: Q[i] * c ([hf4]); NF4_DQ: Q[i] * c' with the absmax
+ * recovered as c' = q * s2 ([dq], one binary32 product). */
+static float dequant_value(int fmt, int nib, int64_t gi, int64_t n_groups,
+                           const void *scales, const uint8_t *zeros)
 {
     if (fmt == ORC_NF4)
         return orc_nf4_table[nib] * ((const float *)scales)[gi];
+    if (fmt == ORC_NF4_DQ) {
+        const uint8_t *qc = (const uint8_t *)scales;
+        float s2;
+        memcpy(&s2, qc + orc_dq_s2_offset(n_groups) + 4 * (gi / ORC_DQ_BLOCK), 4);
+        float c = (float)qc[gi] * s2;
+        return orc_nf4_table[nib] * c;
+    }
     float s = orc_f16_to_f32(((const uint16_t *)scales)[gi]);
     if (fmt == ORC_INT4_SYM)
         return (float)(nib - 8) * s;
@@ -268,7 +330,8 @@ int orc_dequantize(int fmt, int g, const uint8_t *codes, const void *scales,
         return -1;
     for (int64_t e = 0; e < N * K; ++e) {
         int64_t gi = e / g; /* K % g == 0: flat groups never straddle rows */
-        float v = dequant_value(fmt, get_nibble(codes, e), gi, scales, zeros);
+        float v = dequant_value(fmt, get_nibble(codes, e), gi, N * K / g, scales,
+                                zeros);
         out[e] = out_t == ORC_F16 ? orc_f32_to_f16(v) : orc_f32_to_bf16(v);
     }
     return 0;
@@ -304,7 +367,7 @@ int orc_matmul(int fmt, int g, int act_t, const uint16_t *x, int64_t M,
         for (int64_t k = 0; k < K; ++k) {
             int64_t e = n * K + k;
             float v = dequant_value(fmt, get_nibble(codes, e), n * G + k / g,
-                                    scales, zeros);
+                                    N * G, scales, zeros);
             wrow[k] = act_t == ORC_F16 ? orc_f16_to_f32(orc_f32_to_f16(v))
                                        : orc_bf16_to_f32(orc_f32_to_bf16(v));
         }

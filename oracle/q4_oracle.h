@@ -26,6 +26,16 @@
  *   [hf4]   section "Where the accuracy goes" and [bnb] "INT4 Quantization >
  *           Practical Implementation with bitsandbytes": the matmul runs in the
  *           16-bit compute dtype on dequantized weights.
+ *   [dq]    Double quantization of the NF4 block constants: "Loading a model
+ *           in 4-bit", the configuration flag and the section "Where the
+ *           accuracy goes" (the constants are compressed too, about 0.4 bits
+ *           per parameter saved), and the closing section on NF4 (the
+ *           per-block scales quantized again in blocks of 256 to 8 bits,
+ *           0.5 -> about 0.127 bits per parameter).  The 8-bit code is not
+ *           given: read as symmetric absmax int8 coding (scale = block
+ *           max / 127, nearest level), with a binary32 second-level constant
+ *           per 256 absmax values (8/64 + 32/(64*256) = 0.127 bits at g = 64).
+ *           No mean is subtracted (none is described).
  */
 #ifndef Q4_ORACLE_H
 #define Q4_ORACLE_H
@@ -37,7 +47,10 @@ extern "C" {
 
 /* Format and dtype ids (the same numbering as the product ABI, defined here
  * independently). */
-enum { ORC_NF4 = 0, ORC_INT4_SYM = 1, ORC_INT4_ASYM = 2 };
+enum { ORC_NF4 = 0, ORC_INT4_SYM = 1, ORC_INT4_ASYM = 2, ORC_NF4_DQ = 3 };
+
+/* Double quantization ([dq]): absmax values per second-level block. */
+enum { ORC_DQ_BLOCK = 256 };
 enum { ORC_F16 = 0, ORC_BF16 = 1 };
 
 /* The NF4 codebook as printed (16 binary32 values). */
@@ -60,10 +73,22 @@ void orc_f32_to_bf16_array(const float *in, uint16_t *out, int64_t n);
 int orc_nf4_nearest(float x);
 void orc_nf4_nearest_array(const float *in, uint8_t *out, int64_t n);
 
+/* Second-level quantization of n absmax values c[] ([dq]): per run of
+ * ORC_DQ_BLOCK values, s2[b] = c2 / 127 (c2 the run's max) and
+ * qc[i] = clamp(rint(c[i] / s2), 0, 127), 0 where s2 == 0. */
+void orc_double_quant(const float *c, int64_t n, uint8_t *qc, float *s2);
+
+/* Byte offset of the s2 array in an NF4_DQ scales buffer with n_groups
+ * codes: the codes rounded up to a multiple of 16 bytes. */
+int64_t orc_dq_s2_offset(int64_t n_groups);
+
 /* Quantize a row-major fp16 weight W[N][K] (bit patterns) with groups of g
  * contiguous elements along K.
  *   codes  : uint8[N*K/2], byte t = nib[2t] | nib[2t+1] << 4 (flat order)
- *   scales : NF4 -> float[N*K/g] (absmax), INT4 -> uint16 fp16 bits [N*K/g]
+ *   scales : NF4 -> float[N*K/g] (absmax), INT4 -> uint16 fp16 bits [N*K/g],
+ *            NF4_DQ -> bytes: uint8 qc[N*K/g] (zero-filled up to the next
+ *            multiple of 16), then float s2[ceil(N*K/g / 256)]; the codes are
+ *            those NF4 gives
  *   zeros  : INT4-asym only, uint8[ceil(N*K/g / 2)], zero-points packed two
  *            per byte in flat group order, low nibble first; NULL otherwise.
  * Returns 0, or -1 on a bad argument (K % g != 0, unknown format, ...). */

@@ -380,7 +380,7 @@ def test_dequant_is_deterministic_function_of_codes(orc, fmt):
 
 
 # -------------------------------------------------------------- P8 product
-@pytest.mark.parametrize("fmt,act_t", [(NF4, F16), (SYM, BF16), (ASYM, BF16), (NF4, BF16)])
+@pytest.mark.parametrize("fmt,act_t", [(NF4, F16), (SYM, BF16), (ASYM, BF16), (NF4, BF16), (3, BF16)])
 def test_matmul_reference(orc, fmt, act_t):
     N, K, M, g = 40, 256, 3, 32
     w = _rand_w(N, K, 5 + fmt)
