@@ -163,6 +163,11 @@ def main():
     torch.cuda.synchronize()
     quant_ms = e0.elapsed_time(e1)
     quant_bytes = n_weights * 2 + w_bytes
+    # the same weights with double-quantized absmax (8-bit codes per block,
+    # a binary32 constant per 256 blocks)
+    qw_dq = [[q4.quantize(w, q4.NF4_DQ, 64) for w in mats] for mats in fp16]
+    torch.cuda.synchronize()
+    w_bytes_dq = sum(q.nbytes() for row in qw_dq for q in row)
     del fp16
     torch.cuda.empty_cache()
 
@@ -251,6 +256,19 @@ def main():
             token_single()
         single_ms = timed(graph.replay, reps)
         del graph
+    # double-quantized decode token: same products, chained the same way;
+    # checked against single launches, then timed
+    flat_qd = [q for row in qw_dq for q in row]
+    yd = [torch.empty((1, q.N), dtype=torch.bfloat16, device=dev) for q in flat_qd]
+    tasks_dq = [(x, q, y, q4.TASK_NO_WAIT) for x, q, y in zip(flat_x, flat_qd, yd)]
+    chains_dq = [tasks_dq[i:i + q4.CHAIN_MAX] for i in range(0, len(tasks_dq), q4.CHAIN_MAX)]
+    ref_dq = [q4.gemv(x, q) for x, q in zip(flat_x, flat_qd)]
+    run_chains(chains_dq)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(yd, ref_dq)):
+        raise RuntimeError("double-quantized chain differs from single-product launches")
+    del ref_dq
+    dq_ms = timed(lambda: run_chains(chains_dq), max(args.steps // 2, 3))
     launch_ms = [a.elapsed_time(b) for evs in lev for a, b in evs]
     chain_avg_us = sum(launch_ms) / len(launch_ms) * 1e3
     bytes_per_chain = w_bytes / n_chain
@@ -294,6 +312,15 @@ def main():
             "single_launch_graph_ms_per_step": None if single_ms is None else round(single_ms, 4),
             "single_launch_graph_GBps": None if single_ms is None
             else round(w_bytes / (single_ms * 1e-3) / 1e9, 1),
+            "dq_decode_token": {
+                "format": "NF4 block 64, absmax double-quantized (8-bit codes, binary32 "
+                          "constant per 256 blocks)",
+                "weight_bytes_per_token": w_bytes_dq,
+                "bits_per_weight": round(w_bytes_dq * 8 / n_weights, 4),
+                "ms_per_step": round(dq_ms, 4),
+                "GBps": round(w_bytes_dq / (dq_ms * 1e-3) / 1e9, 1),
+                "speedup_vs_fp32_absmax": round(ms / dq_ms, 3),
+            },
             "quantize_all_ms": round(quant_ms, 3),
             "quantize_all_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
             "device": props.name,

@@ -4,7 +4,9 @@
 // quantization works": unpack the low nibble then the high nibble of each
 // byte and multiply the level by the block scale; "Loading a model in 4-bit",
 // "Block-wise quantisation, stated exactly": w = c * Q[i]): one binary32
-// product per weight, rounded once (nearest-even) to the output dtype.
+// product per weight, rounded once (nearest-even) to the output dtype.  With
+// double-quantized absmax the block's c is first recovered as qc * s2 (one
+// binary32 product).
 //
 // gfx950 mapping: a flat stream.  Each lane decodes one dword of codes (8
 // weights, all in one group since groups are >= 32 weights and aligned) and
@@ -39,11 +41,13 @@ template <int FMT, int OUT>
 __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__restrict__ codes,
                                                             const void *__restrict__ scales,
                                                             const uint8_t *__restrict__ zeros,
+                                                            const float *__restrict__ s2,
                                                             u32x4 *__restrict__ out,
                                                             int64_t n_units, int gshift)
 {
+    constexpr int LF = level_fmt(FMT);
     __shared__ float tbl[16];
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (LF == Q4_NF4) {
         if (threadIdx.x < 16)
             tbl[threadIdx.x] = c_nf4[threadIdx.x];
         __syncthreads();
@@ -68,6 +72,8 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__re
                 cw[u] = codes[unit];
                 if constexpr (FMT == Q4_NF4)
                     sc[u] = ((const float *)scales)[gi];
+                else if constexpr (FMT == Q4_NF4_DQ)  // c' = qc * s2, one product
+                    sc[u] = keep_f32((float)((const uint8_t *)scales)[gi] * s2[gi / kDqRun]);
                 else
                     sc[u] = h2f(((const uint16_t *)scales)[gi]);
                 if constexpr (FMT == Q4_INT4_ASYM)
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__re
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t unit = (t0 + u) * 64 + lane;
             float v[8];
-            if constexpr (FMT == Q4_NF4) {
+            if constexpr (LF == Q4_NF4) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     v[i] = keep_f32(tbl[(cw[u] >> (4 * i)) & 0xf] * sc[u]);
@@ -118,12 +124,17 @@ hipError_t launch_fmt(int gshift, const uint8_t *codes, const void *scales, cons
     if (blocks > cap)
         blocks = cap;
     dim3 grid((unsigned)blocks), block(kBlock);
+    const float *s2 = nullptr;
+    if constexpr (FMT == Q4_NF4_DQ)
+        s2 = (const float *)((const uint8_t *)scales + dq_s2_offset((N * K) >> gshift));
     if (out_t == Q4_F16)
         hipLaunchKernelGGL((dequantize_kernel<FMT, Q4_F16>), grid, block, 0, s,
-                           (const uint32_t *)codes, scales, zeros, (u32x4 *)out, n_units, gshift);
+                           (const uint32_t *)codes, scales, zeros, s2, (u32x4 *)out, n_units,
+                           gshift);
     else
         hipLaunchKernelGGL((dequantize_kernel<FMT, Q4_BF16>), grid, block, 0, s,
-                           (const uint32_t *)codes, scales, zeros, (u32x4 *)out, n_units, gshift);
+                           (const uint32_t *)codes, scales, zeros, s2, (u32x4 *)out, n_units,
+                           gshift);
     return hipGetLastError();
 }
 
@@ -137,6 +148,8 @@ hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const voi
     switch (f) {
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(gshift, codes, scales, zeros, N, K, out_t, out, s);
+    case Q4_NF4_DQ:
+        return launch_fmt<Q4_NF4_DQ>(gshift, codes, scales, zeros, N, K, out_t, out, s);
     case Q4_INT4_SYM:
         return launch_fmt<Q4_INT4_SYM>(gshift, codes, scales, zeros, N, K, out_t, out, s);
     default:

@@ -33,6 +33,9 @@
 //  * Dequantization runs in registers between the MFMAs: INT4 as one exact
 //    fma per weight ((q - z) * s = q * s + (-z * s), both terms exact), NF4
 //    as a byte-indexed LDS table of level pairs and one binary32 multiply.
+//    With double-quantized NF4 absmax the span load brings the 8-bit codes
+//    and the runs' binary32 constants, and each group's absmax is recovered
+//    with one product before the NF4 path.
 //  * W rows are assigned to fragment positions so that each lane's 8 output
 //    values are 8 consecutive columns of y: one 16-byte store per lane per
 //    x-row fragment.
@@ -77,10 +80,14 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 template <int FMT, int G>
 struct Span {
     static constexpr int ng = kSpanK / G;                  // groups per span (8, 4, 2)
-    static constexpr int ss = FMT == Q4_NF4 ? 4 : 2;       // bytes per scale
-    static constexpr int sdw = ng * ss / 4;                // scale dwords per span (1 .. 8)
-    // loads per fragment and span: scales (16 bytes each at most), zero-points
-    static constexpr int nload = (sdw >= 4 ? sdw / 4 : 1) + (FMT == Q4_INT4_ASYM ? 1 : 0);
+    // bytes per scale (double-quantized NF4: the 8-bit absmax code)
+    static constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    // scale dwords per span (1 .. 8)
+    static constexpr int sdw = FMT == Q4_NF4_DQ ? (ng == 8 ? 2 : 1) : ng * ss / 4;
+    // loads per fragment and span: scales (16 bytes each at most), then the
+    // zero-points (asym) or the runs' second-level constants (NF4_DQ)
+    static constexpr int nload =
+        (sdw >= 4 ? sdw / 4 : 1) + (FMT == Q4_INT4_ASYM || FMT == Q4_NF4_DQ ? 1 : 0);
 };
 
 // Per-lane codes of one step: 16 codes per fragment, one dword per 32-deep
@@ -90,7 +97,9 @@ struct WStep {
 };
 
 // Per-lane scales and zero-points of one span, as loaded: the scale dwords
-// of the row's groups and the 64 bits holding its zero-point nibbles.
+// of the row's groups and the 64 bits holding its zero-point nibbles (for
+// double-quantized NF4: the 8-bit absmax codes, and the second-level
+// constants of the run holding the span's first group and of the next run).
 template <int FMT, int G>
 struct MSpan {
     uint32_t s[kNF][Span<FMT, G>::sdw];
@@ -107,7 +116,9 @@ struct TileCtx {
     int rd[2];   // fragment reads: LDS byte offset of half step h (+2048 per fragment)
     int cv;      // codes: voffset of fragment 0 at k = 0
     int sv;      // scales: voffset of fragment 0's row
-    int zv;      // zero-points: voffset of the byte holding fragment 0's row's first nibble
+    int zv;      // zero-points: voffset of the byte holding fragment 0's row's first nibble;
+                 // NF4_DQ: fragment 0's row's first group counted from the start of
+                 // the run holding the tile's first group
     int zo;      // ... and that nibble's position in it (0 or 1)
     int fq;      // lane quad
 };
@@ -161,6 +172,11 @@ __device__ __forceinline__ void load_span(MSpan<FMT, G> &ms, int j, const TileCt
         else
             ms.z[j] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(c.zr, c.zv, ug >> 1, 0), 0u};
     }
+    if constexpr (FMT == Q4_NF4_DQ) {
+        // the span's groups (at most 8) lie in one run or straddle into the
+        // next: both constants, from the run of the first group
+        ms.z[j] = __builtin_amdgcn_raw_buffer_load_b64(c.zr, 4 * ((c.zv + ug) / kDqRun), 0, 0);
+    }
 }
 
 // Scale and exact bias -z * s of fragment j at step sp (0..3) of the span
@@ -176,6 +192,13 @@ __device__ __forceinline__ void wscale(const MSpan<FMT, G> &ms, int j, int sp, c
             s = std::bit_cast<float>(c.fq >= 2 ? ms.s[j][2 * sp + 1] : ms.s[j][2 * sp]);
         else
             s = std::bit_cast<float>(ms.s[j][(64 * sp) / G]);
+        b = 0.0f;
+    } else if constexpr (FMT == Q4_NF4_DQ) {
+        const int e = G == 32 ? 2 * sp + (c.fq >> 1) : (64 * sp) / G;  // group in the span
+        const uint32_t q = (ms.s[j][e >> 2] >> (8 * (e & 3))) & 0xffu;
+        const int first = c.zv + 4 * j * c.Gn + k0 / G;                // span's first group
+        const uint32_t s2 = ((first % kDqRun) + e >= kDqRun) ? ms.z[j][1] : ms.z[j][0];
+        s = keep_f32((float)q * std::bit_cast<float>(s2));  // c' = qc * s2, one product
         b = 0.0f;
     } else {
         uint32_t h;
@@ -265,7 +288,7 @@ __device__ __forceinline__ void kstep(f32x4 (&acc)[kNF][kMF], u32x4 (&wf)[2][kNF
                 wscale<FMT, G>(mo, dj, SP, c, k0, s, b);
             else
                 wscale<FMT, G>(mn, dj, SPN, c, kn, s, b);
-            if constexpr (FMT == Q4_NF4) {
+            if constexpr (level_fmt(FMT) == Q4_NF4) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     lp[i] = ptbl[(src.cw[dj][dh] >> (8 * i)) & 0xffu];
@@ -299,7 +322,7 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
     // reads of one never alias the DMA into the other
     __shared__ __attribute__((aligned(1024))) char xs0[X_BYTES];
     __shared__ __attribute__((aligned(1024))) char xs1[X_BYTES];
-    __shared__ float2 ptbl[FMT == Q4_NF4 ? 256 : 1];
+    __shared__ float2 ptbl[level_fmt(FMT) == Q4_NF4 ? 256 : 1];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -310,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
     const int n0 = (int)(blockIdx.x / (unsigned)mtiles) * BN;
     const int Gn = K / G;
 
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (level_fmt(FMT) == Q4_NF4) {
         if (t < 256)
             ptbl[t] = float2{kNF4[t & 15], kNF4[t >> 4]};
     }
@@ -330,13 +353,20 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
     const int64_t nrows = N - n0 < BN ? N - n0 : BN;
     c.xr = make_rsrc(x + (int64_t)m0 * K, mrows * K * 2);
     c.cr = make_rsrc(codes + (int64_t)n0 * (K >> 1), nrows * (K >> 1));
-    const int64_t s_total = padded_meta_bytes((int64_t)N * Gn * S::ss);
+    const int64_t s_total = FMT == Q4_NF4_DQ ? padded_meta_bytes(dq_scales_bytes((int64_t)N * Gn))
+                                             : padded_meta_bytes((int64_t)N * Gn * S::ss);
     c.sr = make_rsrc((const char *)scales + (int64_t)n0 * Gn * S::ss,
                      s_total - (int64_t)n0 * Gn * S::ss);
     const int64_t zg0 = (int64_t)n0 * Gn;  // flat group index of the tile's first group
     if constexpr (FMT == Q4_INT4_ASYM) {
         const int64_t z_total = padded_meta_bytes(((int64_t)N * Gn + 1) / 2);
         c.zr = make_rsrc(zeros + (zg0 >> 1), z_total - (zg0 >> 1));
+    } else if constexpr (FMT == Q4_NF4_DQ) {
+        // second-level constants from the run of the tile's first group to
+        // the end of the padded buffer (the 8-byte load of the last run
+        // reads into the padding)
+        const int64_t o2 = dq_s2_offset((int64_t)N * Gn) + 4 * (zg0 / kDqRun);
+        c.zr = make_rsrc((const char *)scales + o2, s_total - o2);
     } else {
         c.zr = c.sr;
     }
@@ -354,6 +384,10 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
         const int a = (int)(zg0 & 1) + wrow * Gn;
         c.zv = a >> 1;
         c.zo = a & 1;
+        if constexpr (FMT == Q4_NF4_DQ) {
+            c.zv = (int)(zg0 % kDqRun) + wrow * Gn;
+            c.zo = 0;
+        }
     }
     // x DMA: lane l of 1 KB block B is row 8 B + l / 8, position l % 8,
     // holding chunk (l % 8) ^ (((8 B + l / 8) >> 1) & 7); the row's swizzle
@@ -397,7 +431,7 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
         float s, b;
         float2 lp[4];
         wscale<FMT, G>(mc, j, 0, c, 0, s, b);
-        if constexpr (FMT == Q4_NF4) {
+        if constexpr (level_fmt(FMT) == Q4_NF4) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 lp[i] = ptbl[(wa.cw[j][0] >> (8 * i)) & 0xffu];
@@ -492,6 +526,8 @@ hipError_t launch_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_
     switch (f) {
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
+    case Q4_NF4_DQ:
+        return launch_fmt<Q4_NF4_DQ>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
     case Q4_INT4_SYM:
         return launch_fmt<Q4_INT4_SYM>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
     default:

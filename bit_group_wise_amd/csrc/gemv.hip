@@ -42,6 +42,11 @@
 //    in banks); larger M reads them from L2 step by step.
 //  * Lane partial sums are reduced across the wave with DPP; y is rounded
 //    once to the activation dtype.
+//  * NF4 with double-quantized absmax ("Loading a model in 4-bit", "Where
+//    the accuracy goes"): a chunk's scale is read as its group's 8-bit code
+//    (one byte) and its run's binary32 constant (a dword that the 8 to 32
+//    groups of a row in the same run share, so it comes from cache), and
+//    the absmax is recovered with one product; all else is NF4's path.
 #include <type_traits>
 
 #include "q4_common.hpp"
@@ -75,11 +80,11 @@ enum XSrc { X_GLOBAL = 0, X_LDS = 1, X_REG = 2 };
 template <int FMT, int ACT, int XS>
 struct Cfg {
     // bf16 activations converted to fp16 for NF4 when they are staged
-    static constexpr bool conv_x = FMT == Q4_NF4 && ACT == Q4_BF16 && XS != X_GLOBAL;
+    static constexpr bool conv_x = level_fmt(FMT) == Q4_NF4 && ACT == Q4_BF16 && XS != X_GLOBAL;
     // dot2 operand type
     static constexpr int ct = (ACT == Q4_F16 || conv_x) ? Q4_F16 : Q4_BF16;
     // NF4 in bf16: hi + lo level parts (two table dwords per byte)
-    static constexpr bool pair = FMT == Q4_NF4 && ct == Q4_BF16;
+    static constexpr bool pair = level_fmt(FMT) == Q4_NF4 && ct == Q4_BF16;
 };
 
 __constant__ uint32_t c_parts[3][16] = {
@@ -141,10 +146,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 
 // Buffer views of one weight row n0: its codes, scales and zero-point bytes
-// (empty for n0 >= N, so a position past the last row loads zeros).
+// (empty for n0 >= N, so a position past the last row loads zeros).  With
+// double-quantized absmax, `scales` covers the row's 8-bit absmax codes and
+// s2 points at the second-level constant of the run holding the row's first
+// group (the kernels receive the constants' base in place of `zeros`).
 struct RowViews {
     __amdgpu_buffer_rsrc_t codes, scales, zeros;
-    int zpar;  // parity of the row's first flat group index
+    int zpar;  // parity of the row's first flat group index (asym), or its
+               // position in its run of kDqRun groups (double quantization)
+    const float *s2;
 };
 
 template <int FMT>
@@ -152,17 +162,26 @@ __device__ __forceinline__ RowViews row_views(const uint8_t *codes, const void *
                                               const uint8_t *zeros, int64_t n0, int64_t N,
                                               int64_t row_bytes, int64_t G)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : 2;
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     const bool live = n0 < N;
     RowViews v;
+    v.s2 = nullptr;
     v.codes = make_rsrc(codes + n0 * row_bytes, live ? row_bytes : 0);
     v.scales = make_rsrc((const char *)scales + n0 * G * ss, live ? G * ss : 0);
     const int64_t g0 = n0 * G;
     v.zpar = (int)(g0 & 1);
-    if constexpr (FMT == Q4_INT4_ASYM)
+    if constexpr (FMT == Q4_INT4_ASYM) {
         v.zeros = make_rsrc(zeros + (g0 >> 1), live ? ((g0 + G - 1) >> 1) - (g0 >> 1) + 1 : 0);
-    else
+    } else if constexpr (FMT == Q4_NF4_DQ) {
+        // g0 >= 0: shifts instead of signed division; a row past the end
+        // points at the first constant (read, never used: its codes are 0)
+        const uint64_t ug0 = (uint64_t)g0;
+        v.s2 = (const float *)zeros + (live ? ug0 >> 8 : 0);
+        v.zpar = (int)(ug0 & (kDqRun - 1));
         v.zeros = v.codes;
+    } else {
+        v.zeros = v.codes;
+    }
     return v;
 }
 
@@ -174,6 +193,11 @@ struct Stage {
     u32x4 cw[2];
     float sc[2];
     float zf[2];
+    // double quantization: the constants of the (at most 3) runs of kDqRun
+    // groups the row touches (scalar registers) and the row's first group's
+    // position in the first of them
+    float s2[3];
+    int zpar;
 };
 
 // Chunk of half h of stage s for a lane.
@@ -199,6 +223,9 @@ __device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, 
         if constexpr (FMT == Q4_NF4)
             st.sc[h] = std::bit_cast<float>(
                 __builtin_amdgcn_raw_buffer_load_b32(v.scales, in ? 4 * gl : -16, 0, kNT));
+        else if constexpr (FMT == Q4_NF4_DQ)  // the 8-bit code; the constant below
+            st.sc[h] = std::bit_cast<float>((uint32_t)
+                __builtin_amdgcn_raw_buffer_load_b8(v.scales, in ? gl : -16, 0, kNT));
         else
             st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, in ? 2 * gl : -16, 0, kNT));
         if constexpr (FMT == Q4_INT4_ASYM) {
@@ -209,6 +236,20 @@ __device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, 
         } else {
             st.zf[h] = 0.0f;
         }
+    }
+    if constexpr (FMT == Q4_NF4_DQ) {
+        // One scalar load of the constants of the row's runs (a row of at
+        // most 16384 / 32 groups touches at most 3 runs; the last ones may
+        // read the buffer's padding, never used), rather than a vector load
+        // per stage: the vector memory instructions per stage are what the
+        // loop's rate is most sensitive to.  The group's run is picked when
+        // the stage is computed.
+        typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)v.s2;
+        st.s2[0] = c[0];
+        st.s2[1] = c[1];
+        st.s2[2] = c[2];
+        st.zpar = v.zpar;
     }
 }
 
@@ -281,7 +322,7 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                                               const u32x4 (&xreg)[XS == X_REG ? 8 * MT : 1],
                                               const float (&xinv)[MT][2], __amdgpu_buffer_rsrc_t xr,
                                               int K, int xrow, int s, int lane, int C,
-                                              uint32_t laneoff)
+                                              uint32_t laneoff, int gshift)
 {
     constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
     const uint32_t ones = CT == Q4_BF16 ? 0x3f803f80u : 0x3c003c00u;
@@ -359,7 +400,26 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                 t += PAIR ? p[m][a] + pl[m][a] : p[m][a];
             if constexpr (FMT == Q4_INT4_ASYM)
                 t = __builtin_fmaf(-st.zf[h], sx[m], t);
-            acc[m] = __builtin_fmaf(t, st.sc[h] * xinv[m][h], acc[m]);
+            float sc = st.sc[h];
+            if constexpr (FMT == Q4_NF4_DQ) {
+                // The half's 64 chunks cover at most 64 groups, so at most
+                // two runs: the run of its first group (ra) and the next
+                // (rb), picked per half from wave-uniform values; a lane
+                // takes rb when its group is at or past the run boundary.
+                // Groups are counted from the start of the row's first run.
+                const int u = st.zpar + ((kStageChunks * 32 * s + 64 * 32 * h) >> gshift);
+                const int r0 = u >> 8;                         // 0..2
+                const int thr = 256 * (r0 + 1) - u;            // first lane group in rb
+                const uint32_t a0 = std::bit_cast<uint32_t>(st.s2[0]);
+                const uint32_t a1 = std::bit_cast<uint32_t>(st.s2[1]);
+                const uint32_t a2 = std::bit_cast<uint32_t>(st.s2[2]);
+                const uint32_t ra = r0 == 0 ? a0 : (r0 == 1 ? a1 : a2);
+                const uint32_t rb = r0 == 0 ? a1 : a2;
+                const int lg = (32 * lane) >> gshift;          // the lane's group in the half
+                const float s2 = std::bit_cast<float>(lg >= thr ? rb : ra);
+                sc = keep_f32((float)std::bit_cast<uint32_t>(st.sc[h]) * s2);  // c' = qc * s2
+            }
+            acc[m] = __builtin_fmaf(t, sc * xinv[m][h], acc[m]);
         }
     }
 }
@@ -452,7 +512,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     }
     // NF4 level parts: lane i (mod 16) holds entry i; fetched by lane permutes
     uint32_t part_lo = 0, part_hi = 0;
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (level_fmt(FMT) == Q4_NF4) {
         part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
         if constexpr (F::pair)
             part_hi = c_parts[1][lane & 15];
@@ -503,7 +563,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
         const int e = piece >> 4, h = (piece >> 3) & 1;
         const int n0 = e & 15, n1 = e >> 4;
         uint32_t v;
-        if constexpr (FMT == Q4_NF4) {
+        if constexpr (level_fmt(FMT) == Q4_NF4) {
             // every lane holds the same part variable, so the permute reads
             // entry n of that part; the hi/lo choice is made afterwards
             uint32_t a = (uint32_t)__shfl((int)part_lo, n0), b = (uint32_t)__shfl((int)part_lo, n1);
@@ -571,7 +631,11 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 }
             }
             compute_stage<FMT, F::ct, F::pair, MT, XS>(st[q], acc, tbl, xs, xreg, xinv, xr, K,
-                                                      xrow, cp.s, lane, C, laneoff);
+                                                      xrow, cp.s, lane, C, laneoff, gshift);
+            // (double quantization: keep the refill after the compute, which
+            // the scheduler otherwise hoists at the cost of registers)
+            if constexpr (FMT == Q4_NF4_DQ)
+                __builtin_amdgcn_sched_barrier(0);
             // refill this slot with the position P steps ahead
             pos[q] = advance(pos[(q + P - 1) % P]);
             {
@@ -764,7 +828,7 @@ void gemv_chain_kernel(const ChainArgs a)
     // the level table, by every wave
     {
         uint32_t part_lo = 0, part_hi = 0;
-        if constexpr (FMT == Q4_NF4) {
+        if constexpr (level_fmt(FMT) == Q4_NF4) {
             part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
             if constexpr (F::pair)
                 part_hi = c_parts[1][lane & 15];
@@ -775,7 +839,7 @@ void gemv_chain_kernel(const ChainArgs a)
             const int e = piece >> 4, h = (piece >> 3) & 1;
             const int n0 = e & 15, n1 = e >> 4;
             uint32_t v;
-            if constexpr (FMT == Q4_NF4) {
+            if constexpr (level_fmt(FMT) == Q4_NF4) {
                 uint32_t x0 = (uint32_t)__shfl((int)part_lo, n0), x1 = (uint32_t)__shfl((int)part_lo, n1);
                 if constexpr (F::pair) {
                     const uint32_t c0 = (uint32_t)__shfl((int)part_hi, n0);
@@ -849,8 +913,6 @@ void gemv_chain_kernel(const ChainArgs a)
     } else {
         // ---------------------------------------------------------- compute
         // vector-memory instructions per ring refill
-        constexpr int kLoadsPerStage = FMT == Q4_INT4_ASYM ? 6 : 4;
-        (void)kLoadsPerStage;
         const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * kChainCompute + wave);
         const int total_waves = gridDim.x * kChainCompute;
         // A wave's walk: task by task, its rows of the task and each row's
@@ -953,7 +1015,7 @@ void gemv_chain_kernel(const ChainArgs a)
                 const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
                 compute_stage<FMT, F::ct, F::pair, 1, X_REG>(st[q], acc, tbl, nullptr, xreg, xinv,
                                                            make_rsrc(T.x, 0), T.K, S * kStageXBytes,
-                                                           cp.s, lane, T.K >> 5, laneoff);
+                                                           cp.s, lane, T.K >> 5, laneoff, a.gshift);
                 if (cp.s == S - 1) {
                     const float out = wave_sum(acc[0]);
                     acc[0] = 0.0f;
@@ -1004,6 +1066,10 @@ hipError_t launch_one(const void *x, int M, const uint8_t *codes, const void *sc
     if (blocks > cap)
         blocks = cap;
     constexpr int depth = MT <= 2 ? Q4_GEMV_DEPTH : 2;
+    // double-quantized absmax: the kernel takes the constants' base in
+    // place of the (absent) zero-points
+    if constexpr (FMT == Q4_NF4_DQ)
+        zeros = (const uint8_t *)scales + dq_s2_offset(N * (K >> gshift));
     hipLaunchKernelGGL((gemv_kernel<FMT, ACT, MT, XS, depth>), dim3((unsigned)blocks),
                        dim3(Shape<XS>::block), 0, s, (const uint16_t *)x, M, codes, scales, zeros,
                        (int)N, (int)K, gshift, (uint16_t *)y);
@@ -1061,18 +1127,25 @@ hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_t
                              int ntasks, uint32_t *sync, hipStream_t s)
 {
     ChainArgs a = {};
+    a.gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
     for (int i = 0; i < ntasks; ++i) {
-        a.t[i] = ChainTask{(const uint16_t *)tasks[i].x, tasks[i].codes, tasks[i].scales,
-                           tasks[i].zeros, (uint16_t *)tasks[i].y, (int)tasks[i].N,
-                           (int)tasks[i].K, (tasks[i].flags & Q4_TASK_NO_WAIT) ? 0 : 1};
+        // double-quantized absmax: the constants' base in place of zeros
+        const uint8_t *z = f == Q4_NF4_DQ ? (const uint8_t *)tasks[i].scales +
+                                                dq_s2_offset(tasks[i].N * (tasks[i].K >> a.gshift))
+                                          : tasks[i].zeros;
+        a.t[i] = ChainTask{(const uint16_t *)tasks[i].x, tasks[i].codes, tasks[i].scales, z,
+                           (uint16_t *)tasks[i].y, (int)tasks[i].N, (int)tasks[i].K,
+                           (tasks[i].flags & Q4_TASK_NO_WAIT) ? 0 : 1};
     }
     a.ntasks = ntasks;
-    a.gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
     a.sync = sync;
     const bool bf = act_t == Q4_BF16;
     switch (f) {
     case Q4_NF4:
         return bf ? launch_chain_t<Q4_NF4, Q4_BF16>(a, s) : launch_chain_t<Q4_NF4, Q4_F16>(a, s);
+    case Q4_NF4_DQ:
+        return bf ? launch_chain_t<Q4_NF4_DQ, Q4_BF16>(a, s)
+                  : launch_chain_t<Q4_NF4_DQ, Q4_F16>(a, s);
     case Q4_INT4_SYM:
         return bf ? launch_chain_t<Q4_INT4_SYM, Q4_BF16>(a, s)
                   : launch_chain_t<Q4_INT4_SYM, Q4_F16>(a, s);
@@ -1093,6 +1166,8 @@ hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_
     switch (f) {
     case Q4_NF4:
         return launch_act<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    case Q4_NF4_DQ:
+        return launch_act<Q4_NF4_DQ>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_INT4_SYM:
         return launch_act<Q4_INT4_SYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     default:

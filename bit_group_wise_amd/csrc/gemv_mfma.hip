@@ -25,6 +25,8 @@
 //  * A 2-deep ring of steps keeps the next step's loads in flight.
 //  * The 8 partial 16 x 16 tiles meet in LDS and are summed in wave order
 //    (a fixed order, so the result does not depend on timing).
+//  * Double-quantized NF4 absmax: the lane loads its group's 8-bit code and
+//    its run's binary32 constant and recovers the absmax with one product.
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 #include "q4_mfma.hpp"
@@ -63,7 +65,8 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K, int gshift,
     uint16_t *__restrict__ y)
 {
-    __shared__ float2 ptbl[FMT == Q4_NF4 ? 256 : 1];
+    constexpr int LF = level_fmt(FMT);
+    __shared__ float2 ptbl[LF == Q4_NF4 ? 256 : 1];
     __shared__ f32x4 part[kSkWaves][64];
 
     const int lane = threadIdx.x & 63;
@@ -72,9 +75,9 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const int n0 = blockIdx.x * 16;
     const int G = K >> gshift;
     const int row_bytes = K >> 1;
-    constexpr int ss = FMT == Q4_NF4 ? 4 : 2;
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
 
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (LF == Q4_NF4) {
         if (threadIdx.x < 256)
             ptbl[threadIdx.x] = float2{kNF4[threadIdx.x & 15], kNF4[threadIdx.x >> 4]};
     }
@@ -89,6 +92,13 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     __amdgpu_buffer_rsrc_t zr = sr;
     if constexpr (FMT == Q4_INT4_ASYM)
         zr = sk_rsrc(zeros + (zg0 >> 1), (((int64_t)nrows * G + (zg0 & 1)) + 1) / 2);
+    // double-quantized absmax: the runs' binary32 constants for the block's
+    // groups (zr then starts at the run holding the block's first group)
+    if constexpr (FMT == Q4_NF4_DQ) {
+        const float *s2 = (const float *)((const char *)scales + dq_s2_offset((int64_t)N * G));
+        const int64_t r0 = zg0 / kDqRun, r1 = (zg0 + (int64_t)nrows * G - 1) / kDqRun;
+        zr = sk_rsrc(s2 + r0, 4 * (r1 - r0 + 1));
+    }
     const __amdgpu_buffer_rsrc_t xr = sk_rsrc(x, (int64_t)M * K * 2);
 
     const int nsteps = (K + kSkStep - 1) / kSkStep;
@@ -99,12 +109,17 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
         const int gi = r * G + (k >> gshift);  // group within the block
         if constexpr (FMT == Q4_NF4)
             st.sraw = __builtin_amdgcn_raw_buffer_load_b32(sr, in ? 4 * gi : -16, 0, 0);
+        else if constexpr (FMT == Q4_NF4_DQ)
+            st.sraw = __builtin_amdgcn_raw_buffer_load_b8(sr, in ? gi : -16, 0, 0);
         else
             st.sraw = __builtin_amdgcn_raw_buffer_load_b16(sr, in ? 2 * gi : -16, 0, 0);
         if constexpr (FMT == Q4_INT4_ASYM) {
             const int gz = (int)(zg0 & 1) + gi;
             st.zraw = __builtin_amdgcn_raw_buffer_load_b8(zr, in ? gz >> 1 : -16, 0, 0) >>
                       (4 * (gz & 1));
+        } else if constexpr (FMT == Q4_NF4_DQ) {
+            const int gr = (int)(zg0 % kDqRun) + gi;  // group index from the first run's start
+            st.zraw = __builtin_amdgcn_raw_buffer_load_b32(zr, in ? 4 * (gr / kDqRun) : -16, 0, 0);
         } else {
             st.zraw = 0;
         }
@@ -134,6 +149,9 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
             if constexpr (FMT == Q4_NF4) {
                 s = std::bit_cast<float>(st.sraw);
                 b = 0.0f;
+            } else if constexpr (FMT == Q4_NF4_DQ) {  // c' = qc * s2, one product
+                s = keep_f32((float)st.sraw * std::bit_cast<float>(st.zraw));
+                b = 0.0f;
             } else {
                 s = h2f(st.sraw & 0xffffu);
                 b = FMT == Q4_INT4_SYM ? -8.0f * s : -(float)(st.zraw & 0xfu) * s;
@@ -141,7 +159,7 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 float2 lp[4];
-                if constexpr (FMT == Q4_NF4) {
+                if constexpr (LF == Q4_NF4) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         lp[e] = ptbl[(st.cw[d] >> (8 * e)) & 0xffu];
@@ -205,6 +223,8 @@ hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, i
     switch (f) {
     case Q4_NF4:
         return launch_sk_fmt<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    case Q4_NF4_DQ:
+        return launch_sk_fmt<Q4_NF4_DQ>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_INT4_SYM:
         return launch_sk_fmt<Q4_INT4_SYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     default:

@@ -11,7 +11,10 @@
 
 namespace {
 
-bool format_ok(q4_format f) { return f == Q4_NF4 || f == Q4_INT4_SYM || f == Q4_INT4_ASYM; }
+bool format_ok(q4_format f)
+{
+    return f == Q4_NF4 || f == Q4_INT4_SYM || f == Q4_INT4_ASYM || f == Q4_NF4_DQ;
+}
 bool dtype_ok(q4_dtype t) { return t == Q4_F16 || t == Q4_BF16; }
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -28,7 +31,8 @@ q4_status check_weight(q4_format f, int g, const void *codes, const void *scales
         return Q4_EINVAL;
     if ((f == Q4_INT4_ASYM) != (zeros != nullptr))
         return Q4_EINVAL;
-    if (!aligned(codes, 16) || !aligned(scales, f == Q4_NF4 ? 4 : 2))
+    const uintptr_t sa = f == Q4_NF4_DQ ? 16 : (f == Q4_NF4 ? 4 : 2);
+    if (!aligned(codes, 16) || !aligned(scales, sa))
         return Q4_EALIGN;
     return Q4_OK;
 }
@@ -54,6 +58,8 @@ size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g)
 {
     if (!format_ok(f) || !group_ok(g) || N <= 0 || K <= 0 || K % g != 0)
         return 0;
+    if (f == Q4_NF4_DQ)
+        return pad16(q4::dq_scales_bytes(N * (K / g)));
     return pad16(N * (K / g) * (f == Q4_NF4 ? 4 : 2));
 }
 

@@ -31,6 +31,10 @@ inline constexpr float kNF4[16] = {-1.0f,  -0.696f, -0.525f, -0.395f, -0.284f, -
                                    -0.091f, 0.0f,   0.079f,  0.161f,  0.246f,  0.338f,
                                    0.441f,  0.562f, 0.720f,  1.0f};
 
+// NF4 with double-quantized absmax decodes as NF4 once each block's absmax
+// has been recovered: the level arithmetic of a format.
+constexpr int level_fmt(int f) { return f == Q4_NF4_DQ ? Q4_NF4 : f; }
+
 // Compile-time IEEE helpers (finite inputs only).
 constexpr uint32_t f32_bits(float f) { return std::bit_cast<uint32_t>(f); }
 constexpr float bits_f32(uint32_t u) { return std::bit_cast<float>(u); }

@@ -21,6 +21,18 @@ __host__ __device__ constexpr int64_t padded_meta_bytes(int64_t n)
     return (n + 16 + 15) & ~(int64_t)15;
 }
 
+// NF4_DQ scales buffer: byte offset of the float32 second-level constants
+// (one per kDqRun groups, flat order) after the n_groups 8-bit codes.
+constexpr int kDqRun = 256;
+__host__ __device__ constexpr int64_t dq_s2_offset(int64_t n_groups)
+{
+    return (n_groups + 15) & ~(int64_t)15;
+}
+__host__ __device__ constexpr int64_t dq_scales_bytes(int64_t n_groups)
+{
+    return dq_s2_offset(n_groups) + 4 * ((n_groups + kDqRun - 1) / kDqRun);
+}
+
 hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t K,
                            uint8_t *codes, void *scales, uint8_t *zeros, hipStream_t s);
 hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const void *scales,

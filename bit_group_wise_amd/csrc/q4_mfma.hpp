@@ -32,12 +32,13 @@ __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, f32x4 c)
 }
 
 // Dequantize the 8 weights of one code dword into four 16-bit pairs.  For
-// NF4 the level pairs lp (one per code byte) come from the LDS table.
+// NF4 (also with double-quantized absmax, s then being the recovered absmax)
+// the level pairs lp (one per code byte) come from the LDS table.
 template <int FMT, int ACT>
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float bias, const float2 (&lp)[4])
 {
     float v[8];
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (level_fmt(FMT) == Q4_NF4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = keep_f32(lp[i].x * s);

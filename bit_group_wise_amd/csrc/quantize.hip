@@ -18,6 +18,10 @@
 // IEEE quotient for every pair of fp16 operands with s > 0 (checked
 // exhaustively on all such pairs); NF4 codes come from a 33-bucket table of
 // exact decision thresholds held in LDS.
+//
+// NF4 with double-quantized absmax (the same page, "Where the accuracy
+// goes", and its closing section on NF4: the block constants coded again in
+// runs of 256 to 8 bits) runs one workgroup per run, see quantize_dq_kernel.
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 
@@ -58,6 +62,25 @@ __device__ __forceinline__ float group_min(float v)
     for (int d = 1; d < LPG; d <<= 1)
         v = fminf(v, __shfl_xor(v, d));
     return v;
+}
+
+// NF4 codes of 8 weights of a group with absmax c > 0, as one dword (low
+// nibble first).
+__device__ __forceinline__ uint32_t nf4_word(const float (&v)[8], float c, const NF4Bucket *lut)
+{
+    const float r = 1.0f / c;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = div_mk(v[i], c, r);
+        // |x| <= 1, so b <= 32; the min only guards inputs that break the
+        // finite-input precondition
+        const uint32_t b = min((uint32_t)((x + 1.0f) * 16.0f), 32u);
+        const NF4Bucket e = lut[b];
+        const uint32_t code = e.base + (x >= e.thr ? 1u : 0u);
+        word |= code << (4 * i);
+    }
+    return word;
 }
 
 template <int FMT, int G>
@@ -105,21 +128,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
                 for (int i = 0; i < 8; ++i)
                     a = fmaxf(a, fabsf(v[i]));
                 const float c = group_max<LPG>(a);
-                if (c != 0.0f) {
-                    const float r = 1.0f / c;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float x = div_mk(v[i], c, r);
-                        // |x| <= 1, so b <= 32; the min only guards inputs
-                        // that break the finite-input precondition
-                        const uint32_t b = min((uint32_t)((x + 1.0f) * 16.0f), 32u);
-                        const NF4Bucket e = lut[b];
-                        const uint32_t code = e.base + (x >= e.thr ? 1u : 0u);
-                        word |= code << (4 * i);
-                    }
-                } else {
-                    word = 0x77777777u;
-                }
+                word = c != 0.0f ? nf4_word(v, c, lut) : 0x77777777u;
                 if (in && leader)
                     ((float *)scales)[gi] = c;
             } else if constexpr (FMT == Q4_INT4_SYM) {
@@ -184,6 +193,108 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
     }
 }
 
+// NF4 with double-quantized absmax.  A workgroup owns one run of kDqRun
+// groups (flat order): it codes the run's weights as NF4 with each group's
+// exact absmax c, keeps the c values in LDS, then forms the run's binary32
+// constant s2 = max c / 127 and the 8-bit codes rint(c / s2) clamped to
+// 0..127 (one per thread).  The quotient c / s2 is the correctly rounded IEEE
+// division (the compiler's default for '/').
+template <int G>
+__global__ __launch_bounds__(kBlock) void quantize_dq_kernel(const u32x4 *__restrict__ w,
+                                                             uint32_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ qc,
+                                                             float *__restrict__ s2,
+                                                             int64_t n_groups, int64_t s2_off)
+{
+    static_assert(kBlock == kDqRun, "one thread per group of the run");
+    constexpr int LPG = G / 8;
+    __shared__ NF4Bucket lut[33];
+    __shared__ float cs[kDqRun];
+    __shared__ float wmax[kBlock / 64];
+    if (threadIdx.x < 33)
+        lut[threadIdx.x] = c_buckets[threadIdx.x];
+    const int tid = threadIdx.x;
+    cs[tid] = 0.0f;
+    __syncthreads();
+
+    const int64_t gb0 = (int64_t)blockIdx.x * kDqRun;  // the run's first group
+    const int ng = n_groups - gb0 < kDqRun ? (int)(n_groups - gb0) : kDqRun;
+    const int64_t slot0 = gb0 * LPG;
+    const int nsl = ng * LPG;  // 16-byte slots of the run (a multiple of LPG)
+    constexpr int kSteps = kDqRun * LPG / kBlock;  // full-run steps (4, 8, 16)
+    static_assert(kSteps % kUnroll == 0, "whole unrolled rounds");
+    for (int t0 = 0; t0 < kSteps; t0 += kUnroll) {
+        u32x4 raw[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = (t0 + u) * kBlock + tid;
+            raw[u] = i < nsl ? w[slot0 + i] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = (t0 + u) * kBlock + tid;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = h2f(raw[u][k] & 0xffffu);
+                v[2 * k + 1] = h2f(raw[u][k] >> 16);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                a = fmaxf(a, fabsf(v[k]));
+            const float c = group_max<LPG>(a);
+            const uint32_t word = c != 0.0f ? nf4_word(v, c, lut) : 0x77777777u;
+            if (i < nsl) {
+                codes[slot0 + i] = word;
+                if (i % LPG == 0)
+                    cs[i / LPG] = c;
+            }
+        }
+    }
+    __syncthreads();
+
+    // the run's max (absmax values are >= 0; unused slots hold 0)
+    const float c = cs[tid];
+    float m = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+        m = fmaxf(m, __shfl_xor(m, d));
+    if ((tid & 63) == 0)
+        wmax[tid >> 6] = m;
+    __syncthreads();
+    float c2 = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kBlock / 64; ++i)
+        c2 = fmaxf(c2, wmax[i]);
+    const float sc2 = c2 / 127.0f;
+    int q = 0;
+    if (sc2 != 0.0f) {
+        q = (int)__builtin_rintf(c / sc2);
+        q = q < 0 ? 0 : (q > 127 ? 127 : q);
+    }
+    // codes of the run; a short last run also zero-fills the bytes up to s2
+    // (s2_off <= gb0 + kDqRun: both are multiples of 16 and >= n_groups)
+    if (gb0 + tid < s2_off)
+        qc[gb0 + tid] = (uint8_t)(tid < ng ? q : 0);
+    if (tid == 0)
+        s2[blockIdx.x] = sc2;
+}
+
+template <int G>
+hipError_t launch_dq(const void *w, int64_t N, int64_t K, uint8_t *codes, void *scales,
+                     hipStream_t s)
+{
+    const int64_t n_groups = N * K / G;
+    const int64_t runs = (n_groups + kDqRun - 1) / kDqRun;
+    const int64_t off = dq_s2_offset(n_groups);
+    uint8_t *qc = (uint8_t *)scales;
+    hipLaunchKernelGGL((quantize_dq_kernel<G>), dim3((unsigned)runs), dim3(kBlock), 0, s,
+                       (const u32x4 *)w, (uint32_t *)codes, qc, (float *)(qc + off), n_groups,
+                       off);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_fmt(int g, const void *w, int64_t N, int64_t K, uint8_t *codes, void *scales,
                       uint8_t *zeros, hipStream_t s)
@@ -221,6 +332,10 @@ hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t
                            uint8_t *codes, void *scales, uint8_t *zeros, hipStream_t s)
 {
     switch (f) {
+    case Q4_NF4_DQ:
+        return g == 32 ? launch_dq<32>(w, N, K, codes, scales, s)
+                       : (g == 64 ? launch_dq<64>(w, N, K, codes, scales, s)
+                                  : launch_dq<128>(w, N, K, codes, scales, s));
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(g, w, N, K, codes, scales, zeros, s);
     case Q4_INT4_SYM:

@@ -12,9 +12,10 @@ import ctypes
 import os
 import threading
 
-NF4, INT4_SYM, INT4_ASYM = 0, 1, 2
+NF4, INT4_SYM, INT4_ASYM, NF4_DQ = 0, 1, 2, 3
+DQ_RUN = 256  # absmax values per second-level constant (NF4_DQ)
 F16, BF16 = 0, 1
-FORMATS = {"nf4": NF4, "int4_sym": INT4_SYM, "int4_asym": INT4_ASYM}
+FORMATS = {"nf4": NF4, "int4_sym": INT4_SYM, "int4_asym": INT4_ASYM, "nf4_dq": NF4_DQ}
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
 
@@ -119,7 +120,10 @@ def _cuda(t, name):
 
 
 class QuantizedWeight:
-    """Packed codes, scales and (INT4-asym) zero-points of an [N, K] weight."""
+    """Packed codes, scales and (INT4-asym) zero-points of an [N, K] weight.
+
+    For NF4_DQ, `scales` is the flat uint8 buffer of 8-bit absmax codes and
+    second-level constants (see dq_parts)."""
 
     def __init__(self, fmt: int, g: int, N: int, K: int, codes, scales, zeros):
         self.fmt, self.g, self.N, self.K = fmt, g, N, K
@@ -136,13 +140,36 @@ def alloc_quantized(fmt: int, g: int, N: int, K: int, device) -> QuantizedWeight
     if nc == 0 or ns == 0:
         raise Q4Error(EINVAL, "alloc_quantized")
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+    zeros = torch.zeros((nz,), dtype=torch.uint8, device=device)[: (N * (K // g) + 1) // 2] if nz else None
+    if fmt == NF4_DQ:
+        # uint8 qc[N*G], zero bytes to a multiple of 16, float32 s2[runs]
+        scales = torch.zeros((ns,), dtype=torch.uint8, device=device)[: dq_scales_size(N * (K // g))]
+        return QuantizedWeight(fmt, g, N, K, codes, scales, zeros)
     sdt = torch.float32 if fmt == NF4 else torch.float16
     # scale and zero-point storage carries the ABI's padding to 16 bytes;
     # the tensors handed out are views of the meaningful leading part
     es = 4 if fmt == NF4 else 2
     scales = torch.zeros((ns // es,), dtype=sdt, device=device)[: N * (K // g)].view(N, K // g)
-    zeros = torch.zeros((nz,), dtype=torch.uint8, device=device)[: (N * (K // g) + 1) // 2] if nz else None
     return QuantizedWeight(fmt, g, N, K, codes, scales, zeros)
+
+
+def dq_s2_offset(n_groups: int) -> int:
+    """Byte offset of the second-level constants in an NF4_DQ scales buffer."""
+    return (n_groups + 15) // 16 * 16
+
+
+def dq_scales_size(n_groups: int) -> int:
+    """Meaningful bytes of an NF4_DQ scales buffer (without the padding)."""
+    return dq_s2_offset(n_groups) + 4 * ((n_groups + DQ_RUN - 1) // DQ_RUN)
+
+
+def dq_parts(q: QuantizedWeight):
+    """(qc uint8 [N, K/g], s2 float32 [runs]) views of an NF4_DQ weight."""
+    ng = q.N * (q.K // q.g)
+    off = dq_s2_offset(ng)
+    runs = (ng + DQ_RUN - 1) // DQ_RUN
+    return (q.scales[:ng].view(q.N, q.K // q.g),
+            q.scales[off:off + 4 * runs].view(_torch().float32))
 
 
 def quantize(w, fmt: int, g: int, out: QuantizedWeight | None = None) -> QuantizedWeight:

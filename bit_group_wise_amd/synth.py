@@ -53,6 +53,17 @@ def weight_f16_bits(N: int, K: int, seed: int, sigma: float = 0.02, mu: float = 
     return to_f16_bits(v)
 
 
+def weight_rowscaled_f16_bits(N: int, K: int, seed: int, sigma: float = 0.02) -> np.ndarray:
+    """fp16 weight bit patterns [N, K] ~ N(0, sigma^2) with row r scaled by
+    2^((5 r mod 11) - 5) in float32 before the fp16 cast: neighbouring rows
+    differ in magnitude by up to 2^10, so per-block constants differ widely
+    from row to row and from one run of blocks to the next."""
+    v = normal_f32((N, K), seed, sigma, 0.0)
+    e = ((5 * np.arange(N)) % 11 - 5).astype(np.float32)
+    v *= np.exp2(e)[:, None].astype(np.float32)
+    return to_f16_bits(v)
+
+
 def act_bits(M: int, K: int, seed: int, act_t: int) -> np.ndarray:
     """Activation bit patterns [M, K] ~ N(0, 1) in fp16 (F16) or bf16 (BF16)."""
     v = normal_f32((M, K), seed)

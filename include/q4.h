@@ -25,6 +25,13 @@
  *     dequantized as c * Q[i]; "Where the accuracy goes": the layer
  *     dequantizes to the 16-bit compute dtype and runs an ordinary 16-bit
  *     matmul (fp32 accumulation here).
+ *   - Double quantization of the NF4 absmax (Q4_NF4_DQ): the same page's
+ *     double-quantization flag and "Where the accuracy goes" (the block
+ *     constants are compressed as well), and its closing section on NF4 (the
+ *     per-block scales quantized again in blocks of 256 to 8 bits, from 0.5
+ *     to about 0.127 bits per parameter).  The 8-bit coding is not spelled
+ *     out; it is read here as symmetric absmax int8 with a binary32 constant
+ *     per run of 256 absmax values (rules below).
  *
  * Data layout (all row-major, W is [N, K] like a Linear layer's weight):
  *   w       fp16 [N, K]
@@ -32,6 +39,10 @@
  *           low nibble and element 2t+1 in its high nibble.
  *   scales  NF4: float32 [N, K/g] (the block absmax c)
  *           INT4-sym / INT4-asym: fp16 [N, K/g]
+ *           NF4_DQ: bytes.  uint8 qc[N*K/g] (the 8-bit absmax codes in flat
+ *           group order r*(K/g) + j), zero bytes up to the next multiple of
+ *           16, then float32 s2[ceil(N*K/g / 256)] (one per run of 256
+ *           groups in flat order; runs cross row boundaries).
  *   zeros   INT4-asym only: uint8 [ceil(N*K/g / 2)], the integer zero-points
  *           (0..15) of the groups in flat order r*(K/g) + j, two per byte,
  *           low nibble first.  NULL for the other formats.
@@ -47,8 +58,12 @@
  *   ASYM  lo = min(0, min w), hi = max(0, max w); s = fp16((hi - lo) / 15);
  *         z = clamp(rint(-lo / s), 0, 15); nibble = clamp(rint(w / s) + z,
  *         0, 15); s == 0 gives z = 0 and nibble 0.
+ *   NF4_DQ codes exactly as NF4 (with the exact absmax c); then per run of
+ *         256 absmax values, s2 = c2 / 127 with c2 the run's max, and
+ *         qc = clamp(rint(c / s2), 0, 127) (0 where s2 == 0).
  * Dequantize: NF4 Q[i] * c, SYM (nibble - 8) * s, ASYM (nibble - z) * s, one
- * binary32 product rounded once (nearest-even) to fp16 or bf16.
+ * binary32 product rounded once (nearest-even) to fp16 or bf16.  NF4_DQ first
+ * recovers c' = qc * s2 (one binary32 product), then Q[i] * c' as NF4.
  *
  * Conventions:
  *   - Ownership: every buffer is device memory owned by the caller.  The
@@ -61,8 +76,8 @@
  *     crosses the ABI.  Faults inside a kernel surface at the caller's next
  *     synchronisation.
  *   - Alignment: w, codes, x and out must be 16-byte aligned (the kernels
- *     move 16 bytes per lane); scales must be 4-byte (NF4) or 2-byte (INT4)
- *     aligned, y 2-byte aligned.  There is no slow fallback path.
+ *     move 16 bytes per lane); scales must be 4-byte (NF4), 2-byte (INT4) or
+ *     16-byte (NF4_DQ) aligned, y 2-byte aligned.  There is no slow fallback path.
  *   - Preconditions not checked: inputs are finite; output buffers do not
  *     alias inputs; the buffers are at least the sizes q4_*_bytes report.
  */
@@ -76,7 +91,7 @@
 extern "C" {
 #endif
 
-typedef enum { Q4_NF4 = 0, Q4_INT4_SYM = 1, Q4_INT4_ASYM = 2 } q4_format;
+typedef enum { Q4_NF4 = 0, Q4_INT4_SYM = 1, Q4_INT4_ASYM = 2, Q4_NF4_DQ = 3 } q4_format;
 typedef enum { Q4_F16 = 0, Q4_BF16 = 1 } q4_dtype;
 typedef enum {
     Q4_OK = 0,
@@ -95,7 +110,8 @@ typedef enum {
  * caller left it) and no reader uses the padding as values, but q4_gemm's
  * wide loads may read into it, so the whole size must be allocated. */
 size_t q4_codes_bytes(int64_t N, int64_t K);                      /* N*K/2 */
-size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4), padded */
+size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4), padded;
+                                                                      NF4_DQ: qc, s2 as above, padded */
 size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g);  /* asym: ceil(N*K/g / 2), padded; else 0 */
 
 /* Quantize fp16 weights w[N, K] into codes, scales and (asym) zeros.

@@ -84,6 +84,11 @@ def test_size_helpers_invalid():
     assert q4.zeros_bytes(q4.INT4_ASYM, 3, 96, 32) == 32
     assert q4.scales_bytes(q4.INT4_SYM, 3, 96, 32) == 48
     assert q4.scales_bytes(q4.NF4, 1, 128, 64) == 32
+    # NF4_DQ: 9 codes padded to 16, one 4-byte constant, then the padding
+    assert q4.scales_bytes(q4.NF4_DQ, 3, 96, 32) == 48
+    # 1024 groups: 1024 code bytes + 4 constants (0.127 bits per weight) + 16
+    assert q4.scales_bytes(q4.NF4_DQ, 64, 1024, 64) == 1024 + 16 + 16
+    assert q4.dq_scales_size(1024) * 8 / (64 * 1024) == 0.126953125
 
 
 # Fake device addresses: validation never dereferences them and returns
@@ -102,7 +107,9 @@ def call_gemv(fmt=q4.NF4, g=64, act=q4.BF16, x=A, M=1, codes=A, scales=A, zeros=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=3), q4.EUNSUPPORTED),
+    (dict(fmt=4), q4.EUNSUPPORTED),
+    (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),   # NF4_DQ scales need 16 bytes
+    (dict(fmt=q4.NF4_DQ, zeros=A), q4.EINVAL),
     (dict(g=16), q4.EUNSUPPORTED),
     (dict(g=256), q4.EUNSUPPORTED),
     (dict(w=None), q4.EINVAL),
@@ -165,7 +172,9 @@ def test_gemv_task_layout():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=3), q4.EUNSUPPORTED),
+    (dict(fmt=4), q4.EUNSUPPORTED),
+    (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),   # NF4_DQ scales need 16 bytes
+    (dict(fmt=q4.NF4_DQ, zeros=A), q4.EINVAL),
     (dict(g=16), q4.EUNSUPPORTED),
     (dict(act=2), q4.EUNSUPPORTED),
     (dict(n=0), q4.EINVAL),

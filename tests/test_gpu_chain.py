@@ -21,7 +21,8 @@ from _helpers import DEV, TORCH_ACT, assert_product_ok, dev16
 
 pytestmark = pytest.mark.gpu
 
-GROUPS = {q4.NF4: [32, 64, 128], q4.INT4_SYM: [32, 64, 128], q4.INT4_ASYM: [32, 64, 128]}
+GROUPS = {q4.NF4: [32, 64, 128], q4.INT4_SYM: [32, 64, 128], q4.INT4_ASYM: [32, 64, 128],
+          q4.NF4_DQ: [32, 64, 128]}
 
 
 def _weight(N, K, fmt, g, seed, sigma=0.02):
@@ -73,7 +74,7 @@ def _assert_same(outs, ref, tag):
 
 
 @pytest.mark.parametrize("act", [q4.BF16, q4.F16])
-@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM])
+@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ])
 def test_chain_equals_consecutive_gemv(fmt, act):
     for g in GROUPS[fmt]:
         tag = f"fmt{fmt} g{g} act{act}"
@@ -122,7 +123,7 @@ def test_chain_longest():
 
 def test_chain_against_oracle():
     """A chain's outputs within the product tolerance of the fp64 oracle."""
-    for fmt, g, act in [(q4.NF4, 64, q4.BF16), (q4.INT4_ASYM, 32, q4.F16)]:
+    for fmt, g, act in [(q4.NF4, 64, q4.BF16), (q4.INT4_ASYM, 32, q4.F16), (q4.NF4_DQ, 32, q4.BF16)]:
         shapes = [(300, 4096), (64, 8192), (5, 2176)]
         tasks, refs = [], []
         for i, (N, K) in enumerate(shapes):

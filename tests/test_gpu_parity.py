@@ -17,7 +17,7 @@ from _helpers import DEV, TORCH_ACT, assert_product_ok, assert_quant_equal, dev1
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM]
+FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ]
 GS = [32, 64, 128]
 
 
@@ -156,7 +156,7 @@ def test_gemv_special_inputs(fmt, act):
     y = host16(q4.gemv(dev16(x, act), q))
     torch.cuda.synchronize()
     assert np.all(y[2] == 0)                      # zero x gives exactly zero
-    if fmt != q4.NF4:
+    if fmt in (q4.INT4_SYM, q4.INT4_ASYM):
         # integer levels are exact in 16 bits: a one-hot x returns the
         # dequantized weight bit for bit
         assert np.array_equal(y[0], deq[:, 5])
