@@ -698,12 +698,97 @@ constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a s
 constexpr int kChainMaxK = 16384;
 constexpr int kChainLinBytes = 2 * kChainMaxK;  // one buffer of x as loaded
 
-// A wave's position in the chain: task, row and stage along K.
+// A wave's position in the chain: task, row and stage along K; whether the
+// stage is the row's last, and where the row's output goes.
 struct CPos {
     int t, row, s;
+    bool last;
+    uint16_t *yp;
 };
 
 __device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
+
+// The views of one task for the chained kernel: whole arrays (each under
+// 2 GiB, checked on the host), with a row's and a stage's place added as a
+// wave-uniform offset, so that moving to the next row costs a few scalar
+// instructions and no reload of the task's arguments.  Lanes whose chunk is
+// past the row end are sent past the view by kChainOob.
+struct TaskViews {
+    __amdgpu_buffer_rsrc_t codes, scales, zeros;
+    const float *s2;  // double quantization: the second-level constants
+    uint16_t *y;
+    int N, S, C, row_bytes, G;
+};
+constexpr uint32_t kChainOob = 0x80000000u;
+
+template <int FMT>
+__device__ __forceinline__ TaskViews task_views(const ChainTask &T, int gshift)
+{
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    TaskViews v;
+    v.N = T.N;
+    v.row_bytes = T.K >> 1;
+    v.G = T.K >> gshift;
+    v.C = T.K >> 5;
+    v.S = chain_stages(T.K);
+    v.codes = make_rsrc(T.codes, (int64_t)v.N * v.row_bytes);
+    v.scales = make_rsrc(T.scales, (int64_t)v.N * v.G * ss);
+    v.zeros = FMT == Q4_INT4_ASYM ? make_rsrc(T.zeros, ((int64_t)v.N * v.G + 1) / 2) : v.codes;
+    v.s2 = (const float *)T.zeros;
+    v.y = T.y;
+    return v;
+}
+
+// The loads of stage s of row `row` (row == N: past the last row, every load
+// is out of the views and returns zero), as load_stage does with row views.
+template <int FMT>
+__device__ __forceinline__ void load_stage_chain(Stage &st, const TaskViews &tv, int row, int s,
+                                                 int lane, int gshift)
+{
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    const int g0 = row * tv.G;                                // the row's first flat group
+    const int gs = (kStageChunks * 32 * s) >> gshift;          // the stage's first group in the row
+    const int cd_off = row * tv.row_bytes + 16 * kStageChunks * s;
+    const int sc_off = (g0 + gs) * ss;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lc = 64 * h + lane;                         // chunk within the stage
+        const bool in = kStageChunks * s + lc < tv.C;
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(tv.codes, in ? 16 * lc : kChainOob, cd_off,
+                                                         kNT);
+        const int gl = (32 * lc) >> gshift;                    // group within the stage
+        if constexpr (FMT == Q4_NF4)
+            st.sc[h] = std::bit_cast<float>(
+                __builtin_amdgcn_raw_buffer_load_b32(tv.scales, in ? 4 * gl : kChainOob, sc_off, kNT));
+        else if constexpr (FMT == Q4_NF4_DQ)
+            st.sc[h] = std::bit_cast<float>((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                tv.scales, in ? gl : kChainOob, sc_off, kNT));
+        else
+            st.sc[h] = h2f(
+                __builtin_amdgcn_raw_buffer_load_b16(tv.scales, in ? 2 * gl : kChainOob, sc_off, kNT));
+        if constexpr (FMT == Q4_INT4_ASYM) {
+            // nibble g0 + gs + gl; gs is even, so the byte is
+            // (g0 >> 1) + gs / 2 + ((g0 & 1) + gl) / 2
+            const int gz = (g0 & 1) + gl;
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
+                tv.zeros, in ? gz >> 1 : kChainOob, (g0 >> 1) + (gs >> 1), kNT);
+            st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
+        } else {
+            st.zf[h] = 0.0f;
+        }
+    }
+    if constexpr (FMT == Q4_NF4_DQ) {
+        // the constants of the row's runs, as load_stage reads them (a row
+        // past the end reads the first ones, never used)
+        typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+        const float *p = tv.s2 + (row < tv.N ? (g0 >> 8) : 0);
+        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)p;
+        st.s2[0] = c[0];
+        st.s2[1] = c[1];
+        st.s2[2] = c[2];
+        st.zpar = g0 & (kDqRun - 1);
+    }
+}
 
 // s_waitcnt on vector memory only (expcnt and lgkmcnt left at their maxima).
 template <int N>
@@ -919,35 +1004,40 @@ void gemv_chain_kernel(const ChainArgs a)
         // stages.  Task t's rows are dealt to the waves from a rotated
         // start, so that the waves holding one row more than the others
         // differ from task to task.
+        // tv: the views of the newest position's task (positions are made
+        // and loaded in order, so the newest is always the one loaded)
+        TaskViews tv = task_views<FMT>(a.t[0], a.gshift);
         auto first_pos = [&](int t) {
             for (; t < nt; ++t) {
                 const int e =
                     (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
-                if (e < a.t[t].N)
-                    return CPos{t, e, 0};
+                if (e < a.t[t].N) {
+                    tv = task_views<FMT>(a.t[t], a.gshift);
+                    return CPos{t, e, 0, tv.S == 1, tv.y + e};
+                }
             }
-            return CPos{nt, 0, 0};
+            // past the last task: a row past the end of the last views
+            return CPos{nt, tv.N, 0, false, tv.y};
         };
         auto advance = [&](CPos q) {
             if (q.t >= nt)
                 return q;
-            if (++q.s == chain_stages(a.t[q.t].K)) {
+            if (++q.s == tv.S) {
                 q.s = 0;
                 q.row += total_waves;
-                if (q.row >= a.t[q.t].N)
+                q.yp += total_waves;
+                if (q.row >= tv.N)
                     return first_pos(q.t + 1);
             }
+            q.last = q.s == tv.S - 1;
             return q;
         };
-        // Refills are issued unconditionally (past the last task from an
-        // empty view: the loads return zeros) so that the number of loads
-        // in flight is the same on every path and the waits stay partial.
+        // Refills are issued unconditionally (past the last task with every
+        // load out of the views: they return zeros) so that the number of
+        // loads in flight is the same on every path and the waits stay
+        // partial.
         auto load_pos = [&](Stage &st, CPos q) {
-            const bool live = q.t < nt;
-            const ChainTask &T = a.t[live ? q.t : nt - 1];
-            const RowViews v = row_views<FMT>(T.codes, T.scales, T.zeros, live ? q.row : T.N,
-                                              T.N, T.K >> 1, T.K >> a.gshift);
-            load_stage<FMT>(st, v, q.s, lane, a.gshift, T.K >> 5);
+            load_stage_chain<FMT>(st, tv, q.row, q.s, lane, a.gshift);
         };
         CPos pos[P];
         Stage st[P];
@@ -956,7 +1046,7 @@ void gemv_chain_kernel(const ChainArgs a)
         for (int q = 0; q < P; ++q) {
             if (q > 0)
                 pos[q] = advance(pos[q - 1]);
-            st[q] = Stage{{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+            st[q] = Stage{};
             load_pos(st[q], pos[q]);
         }
         __syncthreads();  // the table, the counters and x of task 0
@@ -1005,22 +1095,21 @@ void gemv_chain_kernel(const ChainArgs a)
                     while (cur < cp.t)
                         enter();
                 }
-                const ChainTask &T = a.t[live ? cp.t : nt - 1];
-                const int S = chain_stages(T.K);
                 const int key = 8 * cp.t + cp.s;
                 if (key != xkey) {
                     chain_x_slice(xreg, xinv_reg, xb[cp.t & 1], xinv_lds[cp.t & 1], cp.s, lane);
                     xkey = key;
                 }
                 const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
+                // (x comes from registers: no x view, K or chunk count needed)
                 compute_stage<FMT, F::ct, F::pair, 1, X_REG>(st[q], acc, tbl, nullptr, xreg, xinv,
-                                                           make_rsrc(T.x, 0), T.K, S * kStageXBytes,
-                                                           cp.s, lane, T.K >> 5, laneoff, a.gshift);
-                if (cp.s == S - 1) {
+                                                           make_rsrc(nullptr, 0), 0, 0, cp.s, lane,
+                                                           0, laneoff, a.gshift);
+                if (cp.last) {
                     const float out = wave_sum(acc[0]);
                     acc[0] = 0.0f;
                     if (live && lane == 0)
-                        T.y[cp.row] = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                        *cp.yp = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
                 }
                 pos[q] = advance(pos[(q + P - 1) % P]);
                 load_pos(st[q], pos[q]);

@@ -190,6 +190,8 @@ q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *
             return Q4_EINVAL;
         if (t.K > Q4_GEMV_CHAIN_MAX_K || !q4::gemv_chain_k_ok(t.K))
             return Q4_EUNSUPPORTED;
+        if (t.N * (t.K / 2) > Q4_GEMV_CHAIN_MAX_CODES)  // 32-bit offsets into one view
+            return Q4_EUNSUPPORTED;
     }
     return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
 }

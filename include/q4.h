@@ -162,7 +162,8 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
  * every weight once).
  *
  * ntasks is 1..Q4_GEMV_CHAIN_MAX; each K must satisfy K <= Q4_GEMV_CHAIN_MAX_K
- * (else Q4_EUNSUPPORTED); N and K are checked as in q4_gemv.  `sync` is a
+ * and each task's codes N*K/2 <= Q4_GEMV_CHAIN_MAX_CODES bytes (else
+ * Q4_EUNSUPPORTED); N and K are checked as in q4_gemv.  `sync` is a
  * device buffer of Q4_GEMV_CHAIN_SYNC_BYTES, 16-byte aligned, zeroed by the
  * caller before its first use: the kernel returns words 0 and 1 to zero when
  * it ends, so the buffer can be reused without clearing by later chains on
@@ -173,6 +174,7 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
  * workgroup per compute unit: a launch the runtime refuses returns Q4_EHIP. */
 #define Q4_GEMV_CHAIN_MAX 64
 #define Q4_GEMV_CHAIN_MAX_K 16384
+#define Q4_GEMV_CHAIN_MAX_CODES 2147483519LL /* 2^31 - 129 */
 #define Q4_GEMV_CHAIN_SYNC_BYTES 16
 #define Q4_TASK_NO_WAIT 1u /* x is not written by earlier tasks: no grid-wide wait */
 typedef struct {
