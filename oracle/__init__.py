@@ -21,6 +21,9 @@ pages on 4-bit group-wise quantization):
   contiguous blocks, absmax per block, nearest of 16 entries after dividing by
   the absmax, dequantize = absmax times table value; "Where the accuracy goes":
   the product is an ordinary 16-bit matmul on dequantized weights.
+* "What is 4-bit quantization and why does it matter?", "QLoRA fine-tunes in
+  4-bit": the backward product through the frozen dequantized weights,
+  dX = dY . What (matmul_dx).
 * Double quantization of the NF4 block constants ("Loading a model in 4-bit",
   the double-quantization flag and "Where the accuracy goes"; the closing
   section on NF4: blocks of 256 constants to 8 bits, 0.5 -> about 0.127 bits
@@ -83,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                      _i64, _i64, _i64p, _i64, _f64p, _f64p]
             for f in (L.orc_quantize, L.orc_dequantize, L.orc_matmul):
                 f.restype = _int
+            L.orc_matmul_dx.argtypes = [_int, _int, _int, _u16p, _i64, _u8p, _vp, _u8p,
+                                        _i64, _i64, _i64p, _i64, _f64p, _f64p]
+            L.orc_matmul_dx.restype = _int
             L.orc_double_quant.argtypes = [_f32p, _i64, _u8p, _f32p]
             L.orc_double_quant.restype = None
             L.orc_dq_s2_offset.argtypes = [_i64]
@@ -245,6 +251,37 @@ def matmul(fmt: int, g: int, act_t: int, x_bits, codes, scales, zeros, N: int, K
     if rc != 0:
         raise ValueError("orc_matmul rejected its arguments")
     return y, ad
+
+
+def matmul_dx(fmt: int, g: int, act_t: int, dy_bits, codes, scales, zeros, N: int, K: int,
+              cols=None):
+    """fp64 reference dx = dy . what on columns `cols` of W (all if None).
+
+    dy_bits: uint16 [M, N] in dtype act_t.  Returns (dx float64 [M, ncols],
+    absdot float64 [M, ncols])."""
+    _check_g(g)
+    dy = np.ascontiguousarray(dy_bits, dtype=np.uint16)
+    if dy.ndim == 1:
+        dy = dy[None, :]
+    M = dy.shape[0]
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales)
+    z = np.ascontiguousarray(zeros, dtype=np.uint8) if zeros is not None else None
+    if cols is None:
+        c = None
+        ncols = K
+    else:
+        c = np.ascontiguousarray(cols, dtype=np.int64)
+        ncols = c.size
+    dx = np.empty((M, ncols), dtype=np.float64)
+    ad = np.empty((M, ncols), dtype=np.float64)
+    rc = lib().orc_matmul_dx(fmt, g, act_t, _p(dy, _u16p), M, _p(codes, _u8p),
+                             scales.ctypes.data_as(_vp), _p(z, _u8p) if z is not None else None,
+                             N, K, _p(c, _i64p) if c is not None else None, ncols,
+                             _p(dx, _f64p), _p(ad, _f64p))
+    if rc != 0:
+        raise ValueError("orc_matmul_dx rejected its arguments")
+    return dx, ad
 
 
 def tolerance(absdot: np.ndarray) -> np.ndarray:

@@ -416,3 +416,57 @@ void orc_nf4_nearest_array(const float *in, uint8_t *out, int64_t n)
     for (int64_t i = 0; i < n; ++i)
         out[i] = (uint8_t)orc_nf4_nearest(in[i]);
 }
+
+/* [n4n] "QLoRA fine-tunes in 4-bit": the gradient reaches the layer input
+ * through the dequantized weights, which stay fixed.  Reference
+ * dx[m][j] = sum_n dy[m][n] * what[n][cols[j]] in binary64, summed in n
+ * order, with what rounded to the activation dtype as in orc_matmul;
+ * absdot[m][j] = sum_n |dy[m][n] * what[n][cols[j]]|.  cols == NULL means
+ * columns 0..K-1 (ncols must then equal K). */
+int orc_matmul_dx(int fmt, int g, int act_t, const uint16_t *dy, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, const int64_t *cols, int64_t ncols,
+                  double *dx, double *absdot)
+{
+    if (!valid_shape(fmt, g, N, K) || !dy || M <= 0 || !codes || !scales || !dx)
+        return -1;
+    if ((fmt == ORC_INT4_ASYM) != (zeros != NULL))
+        return -1;
+    if (act_t != ORC_F16 && act_t != ORC_BF16)
+        return -1;
+    if (cols == NULL && ncols != K)
+        return -1;
+    double *wcol = (double *)malloc((size_t)N * sizeof(double));
+    if (!wcol)
+        return -1;
+    int64_t G = K / g;
+    for (int64_t j = 0; j < ncols; ++j) {
+        int64_t k = cols ? cols[j] : j;
+        if (k < 0 || k >= K) {
+            free(wcol);
+            return -1;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t e = n * K + k;
+            float v = dequant_value(fmt, get_nibble(codes, e), n * G + k / g,
+                                    N * G, scales, zeros);
+            wcol[n] = act_t == ORC_F16 ? orc_f16_to_f32(orc_f32_to_f16(v))
+                                       : orc_bf16_to_f32(orc_f32_to_bf16(v));
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                uint16_t b = dy[m * N + n];
+                double yv = act_t == ORC_F16 ? orc_f16_to_f32(b) : orc_bf16_to_f32(b);
+                double p = yv * wcol[n]; /* exact: two 16-bit significands */
+                acc += p;
+                aacc += fabs(p);
+            }
+            dx[m * ncols + j] = acc;
+            if (absdot)
+                absdot[m * ncols + j] = aacc;
+        }
+    }
+    free(wcol);
+    return 0;
+}

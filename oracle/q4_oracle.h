@@ -36,6 +36,9 @@
  *           max / 127, nearest level), with a binary32 second-level constant
  *           per 256 absmax values (8/64 + 32/(64*256) = 0.127 bits at g = 64).
  *           No mean is subtracted (none is described).
+ *   [n4n]   section "QLoRA fine-tunes in 4-bit": in QLoRA the 4-bit base
+ *           weights stay frozen and the gradient passes through the
+ *           dequantized weights, i.e. dX = dY . What (orc_matmul_dx).
  */
 #ifndef Q4_ORACLE_H
 #define Q4_ORACLE_H
@@ -111,6 +114,17 @@ int orc_matmul(int fmt, int g, int act_t, const uint16_t *x, int64_t M,
                const uint8_t *codes, const void *scales, const uint8_t *zeros,
                int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
                double *y, double *absdot);
+
+/* Backward product through the dequantized weights ([n4n] "QLoRA fine-tunes
+ * in 4-bit": gradients flow through the dequantized weights, which do not
+ * change): dx[m][j] = sum_n dy[m][n] * what[n][cols[j]] in binary64 (n
+ * order), what rounded to act_t as in orc_matmul; dy is [M][N] act_t bits;
+ * absdot as in orc_matmul.  cols == NULL means columns 0..K-1.  Returns 0 or
+ * -1. */
+int orc_matmul_dx(int fmt, int g, int act_t, const uint16_t *dy, int64_t M,
+                  const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                  int64_t N, int64_t K, const int64_t *cols, int64_t ncols,
+                  double *dx, double *absdot);
 
 #ifdef __cplusplus
 }
