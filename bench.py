@@ -71,7 +71,7 @@ def parse():
                    help="time budget of the CPU-oracle sample")
     p.add_argument("--skip-extra", action="store_true",
                    help="time only the decode token (for profiler runs)")
-    p.add_argument("--only", choices=["gemm", "quantize", "dequantize", "copy"],
+    p.add_argument("--only", choices=["gemm", "gemm_dx", "quantize", "dequantize", "copy"],
                    help="run one leg alone, a few times, and print its timing "
                         "(for profiler runs); 'copy' is a plain 1 GiB device copy, the "
                         "reference for scaling HBM byte counters")
@@ -393,6 +393,12 @@ def one_leg(leg, torch, q4, dev, stream):
         ms = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 5)
         nb = N * K * 2 + q.nbytes()
         return {"leg": leg, "ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    if leg == "gemm_dx":
+        dy = torch.randn((M, N), device=dev).to(torch.bfloat16)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: q4.gemm_dx(dy, q, out=dx), 5)
+        return {"leg": leg, "ms": round(ms, 4),
+                "TFLOPs": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ms = timed(lambda: q4.gemm(x, q, out=y), 5)
     return {"leg": "gemm", "ms": round(ms, 4),
@@ -511,7 +517,24 @@ def extra_legs(torch, q4, dev, stream):
         torch.matmul(x16, o16.t(), out=y16)
     u16 = timed(unfused16, 20)
     f16t = timed(lambda: q4.gemv(x16, q16, out=y16), 20)
+    # the backward product through the same frozen weight (QLoRA's dX):
+    # dY [2048, 14336] . What -> [2048, 4096], and the unfused equivalent
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(403)
+    dy = torch.empty((M, N), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
+    dy = dy.to(torch.bfloat16)
+    dxo = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    bt = timed(lambda: q4.gemm_dx(dy, q, out=dxo), 10)
+
+    def unfused_dx():
+        q4.dequantize(q, torch.bfloat16, out=out)
+        torch.matmul(dy, out, out=dxo)
+    but = timed(unfused_dx, 10)
     return {
+        "gemm_dx": {"shape": f"dY {M}x{N} . W {N}x{K} int4_asym g32 bf16", "ms": round(bt, 4),
+                    "TFLOPs": round(flops / (bt * 1e-3) / 1e12, 1),
+                    "pct_bf16_peak": round(100 * flops / (bt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1),
+                    "unfused_dequant_then_hipblaslt_ms": round(but, 4)},
         "gemm": {"shape": f"M={M} N={N} K={K} int4_asym g32 bf16", "ms": round(gt, 4),
                  "TFLOPs": round(flops / (gt * 1e-3) / 1e12, 1),
                  "pct_bf16_peak": round(100 * flops / (gt * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)},

@@ -169,6 +169,21 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                                     (hipStream_t)stream));
 }
 
+q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t M,
+                     const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                     int64_t N, int64_t K, void *dx, void *stream)
+{
+    q4_status st = check_product(f, g, act_t, dy, M, codes, scales, zeros, N, K, dx);
+    if (st != Q4_OK)
+        return st;
+    if (N % 8 != 0 || N > Q4_GEMM_DX_MAX_N || N * (K / 2) > Q4_GEMV_CHAIN_MAX_CODES)
+        return Q4_EUNSUPPORTED;
+    if (!aligned(dx, 16))
+        return Q4_EALIGN;
+    return from_hip(q4::launch_gemm_dx(f, g, act_t, dy, M, codes, scales, zeros, N, K, dx,
+                                       (hipStream_t)stream));
+}
+
 q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
                         int ntasks, uint32_t *sync, void *stream)
 {

@@ -49,6 +49,10 @@ hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, i
 bool gemv_chain_k_ok(int64_t K);
 hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
                              int ntasks, uint32_t *sync, hipStream_t s);
+// Backward product dX = dY . What (QLoRA's gradient through the frozen weights).
+hipError_t launch_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t M,
+                          const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                          int64_t N, int64_t K, void *dx, hipStream_t s);
 hipError_t launch_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                        const uint8_t *codes, const void *scales, const uint8_t *zeros,
                        int64_t N, int64_t K, void *y, hipStream_t s);

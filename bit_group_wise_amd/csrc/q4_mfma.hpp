@@ -31,13 +31,14 @@ __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, f32x4 c)
                                                       std::bit_cast<f16x8>(b), c, 0, 0, 0);
 }
 
-// Dequantize the 8 weights of one code dword into four 16-bit pairs.  For
-// NF4 (also with double-quantized absmax, s then being the recovered absmax)
-// the level pairs lp (one per code byte) come from the LDS table.
-template <int FMT, int ACT>
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float bias, const float2 (&lp)[4])
+// The 8 weights of one code dword as binary32 values (element i of the
+// dword in v[i]), each the product q4_dequantize rounds.  For NF4 (also with
+// double-quantized absmax, s then being the recovered absmax) the level
+// pairs lp (one per code byte) come from the LDS table.
+template <int FMT>
+__device__ __forceinline__ void dequant8_f32(uint32_t w, float s, float bias, const float2 (&lp)[4],
+                                             float (&v)[8])
 {
-    float v[8];
     if constexpr (level_fmt(FMT) == Q4_NF4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -56,6 +57,14 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float bias, const
         v[6] = __builtin_fmaf(ubyte_f32<3>(lo), s, bias);
         v[7] = __builtin_fmaf(ubyte_f32<3>(hi), s, bias);
     }
+}
+
+// The same 8 weights rounded to the activation dtype, as four 16-bit pairs.
+template <int FMT, int ACT>
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float bias, const float2 (&lp)[4])
+{
+    float v[8];
+    dequant8_f32<FMT>(w, s, bias, lp, v);
     return u32x4{pack2<ACT>(v[0], v[1]), pack2<ACT>(v[2], v[3]), pack2<ACT>(v[4], v[5]),
                  pack2<ACT>(v[6], v[7])};
 }

@@ -31,6 +31,7 @@ SIGNATURES = {
     "q4_dequantize": (_int, [_int, _int, _vp, _vp, _vp, _i64, _i64, _int, _vp, _vp]),
     "q4_gemv": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "q4_gemm": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "q4_gemm_dx": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "q4_gemv_chain": (_int, [_int, _int, _int, ctypes.c_void_p, _int, _vp, _vp]),
     "q4_status_str": (ctypes.c_char_p, [_int]),
 }
@@ -225,6 +226,24 @@ def gemv(x, q: QuantizedWeight, out=None):
 def gemm(x, q: QuantizedWeight, out=None):
     """y = x . What^T for any M (q4_gemm, matrix cores)."""
     return _product("q4_gemm", x, q, out)
+
+
+def gemm_dx(dy, q: QuantizedWeight, out=None):
+    """dX = dY . What for dY [M, N] (q4_gemm_dx): the gradient through the
+    frozen quantized weight, on the matrix cores."""
+    torch = _torch()
+    _cuda(dy, "dy")
+    if dy.dim() != 2 or dy.shape[1] != q.N:
+        raise ValueError("dy must be [M, N]")
+    act = _act_code(dy.dtype)
+    M = dy.shape[0]
+    if out is None:
+        out = torch.empty((M, q.K), dtype=dy.dtype, device=dy.device)
+    _cuda(out, "out")
+    st = lib().q4_gemm_dx(q.fmt, q.g, act, _ptr(dy), M, _ptr(q.codes), _ptr(q.scales),
+                          _ptr(q.zeros), q.N, q.K, _ptr(out), _stream_ptr(dy))
+    _check(st, "q4_gemm_dx")
+    return out
 
 
 def chain_sync(device):

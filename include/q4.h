@@ -149,6 +149,21 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
                   int64_t N, int64_t K, void *y, void *stream);
 
+/* Backward product through the frozen 4-bit weight, dX[M, K] = dY[M, N] .
+ * What[N, K]: the gradient with respect to the layer input when the base
+ * weights are quantized and frozen and only adapters train ("What is 4-bit
+ * quantization and why does it matter?", "QLoRA fine-tunes in 4-bit": the
+ * gradient flows through the dequantized weights, which never change).  Each
+ * weight value is the one q4_dequantize writes in act_t; the products run on
+ * the matrix cores with fp32 accumulation and dX is rounded once to act_t.
+ * dy is [M, N], dx is [M, K], both act_t, row-major, 16-byte aligned.
+ * Requires N % 8 == 0 (16-byte aligned dY rows), N <= Q4_GEMM_DX_MAX_N and
+ * codes N*K/2 <= Q4_GEMV_CHAIN_MAX_CODES bytes, else Q4_EUNSUPPORTED. */
+#define Q4_GEMM_DX_MAX_N 4194303
+q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t M,
+                     const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                     int64_t N, int64_t K, void *dx, void *stream);
+
 /* A chain of decode GEMVs in one launch.  Each task is one M = 1 product
  * y[1, N] = x[1, K] . What^T with the layout and alignment rules of q4_gemv;
  * all tasks share the format, group size and activation dtype.  The tasks run

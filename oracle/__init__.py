@@ -284,6 +284,22 @@ def matmul_dx(fmt: int, g: int, act_t: int, dy_bits, codes, scales, zeros, N: in
     return dx, ad
 
 
-def tolerance(absdot: np.ndarray) -> np.ndarray:
-    """Per-output bound for a GEMV/GEMM result: 2e-3 * sum|x*what| + 1e-3."""
-    return 2e-3 * absdot + 1e-3
+def half_ulp(v: np.ndarray, act_t: int) -> np.ndarray:
+    """Half the spacing of the fp16 (F16) or bf16 (BF16) numbers at |v|: the
+    largest error of rounding v to that dtype (normal range; the subnormal
+    spacing below it)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    mant, emin = (10, -14) if act_t == F16 else (7, -126)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** emin)))
+    return 2.0 ** (e - mant - 1)
+
+
+def tolerance(absdot: np.ndarray, y_ref=None, act_t=None) -> np.ndarray:
+    """Per-output bound for a GEMV/GEMM result: 2e-3 * sum|x*what| + 1e-3,
+    plus, when the reference and the output dtype are given, half an ulp of
+    the reference in that dtype (the output is rounded once to the
+    activation dtype, which no implementation can avoid)."""
+    t = 2e-3 * absdot + 1e-3
+    if y_ref is not None:
+        t = t + half_ulp(y_ref, act_t)
+    return t

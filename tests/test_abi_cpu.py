@@ -192,3 +192,23 @@ def test_gemv_task_layout():
 ])
 def test_chain_rejects(kw, status):
     assert call_chain(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=12), q4.EUNSUPPORTED),                 # N % 8 != 0
+    (dict(N=8 * 524288), q4.EUNSUPPORTED),         # N above Q4_GEMM_DX_MAX_N
+    (dict(N=65536, K=65536), q4.EUNSUPPORTED),     # codes above 2 GiB - 129
+    (dict(dy=None), q4.EINVAL),
+    (dict(dx=None), q4.EINVAL),
+    (dict(dx=0x10008), q4.EALIGN),                 # dx needs 16 bytes
+    (dict(dy=MIS), q4.EALIGN),
+    (dict(fmt=q4.INT4_ASYM), q4.EINVAL),           # asym without zeros
+    (dict(act=2), q4.EUNSUPPORTED),
+])
+def test_gemm_dx_rejects(kw, status):
+    a = dict(fmt=q4.NF4, g=64, act=q4.BF16, dy=A, M=4, codes=A, scales=A, zeros=None, N=16,
+             K=128, dx=A)
+    a.update(kw)
+    L = q4.lib()
+    assert L.q4_gemm_dx(a["fmt"], a["g"], a["act"], a["dy"], a["M"], a["codes"], a["scales"],
+                        a["zeros"], a["N"], a["K"], a["dx"], None) == status

@@ -427,3 +427,20 @@ def test_oracle_bits_per_weight(orc):
     assert bits[NF4] - 4 == nf["printed_bits"] == nf["absmax_bits"] / nf["block"]
     assert bits[SYM] == 4.125
     assert bits[ASYM] == 4.625
+
+
+def test_output_rounding_term(orc):
+    """The tolerance's output-rounding term is half the spacing of the
+    output dtype at the reference: bf16 spacing at [8, 16) is 2^-4, fp16
+    spacing at [1, 2) is 2^-10; and it is the largest error of that
+    rounding (torch's conversion, checked on a sweep)."""
+    assert orc.half_ulp(np.array([8.03]), BF16)[0] == 2.0 ** -5
+    assert orc.half_ulp(np.array([1.5]), F16)[0] == 2.0 ** -11
+    # (float32 inputs: one rounding, as the kernels' fp32 accumulators get)
+    v = (np.random.default_rng(3).standard_normal(20000) * 50).astype(np.float32)
+    for act, dt in ((BF16, torch.bfloat16), (F16, torch.float16)):
+        r = torch.from_numpy(v).to(dt).double().numpy()
+        assert np.all(np.abs(r - v) <= orc.half_ulp(v, act))
+    t0 = orc.tolerance(np.array([1.0]))
+    t1 = orc.tolerance(np.array([1.0]), np.array([8.03]), BF16)
+    assert t0[0] == 2e-3 + 1e-3 and t1[0] == t0[0] + 2.0 ** -5
