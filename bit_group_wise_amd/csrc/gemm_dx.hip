@@ -10,22 +10,30 @@
 // accumulation and dX is rounded once to the activation dtype.
 //
 // gfx950 mapping:
-//  * The contraction runs over the weight's rows (N), so a matrix-core lane,
-//    which needs 8 consecutive contraction values, would need 8 rows of the
-//    packed layout.  The weight tile of a step (64 rows x 128 columns) is
-//    therefore dequantized into LDS transposed: entry (k, n) of a row of
-//    What^T holds weights n and n + 1 as a 16-bit pair.  A thread
-//    dequantizes one code dword (8 columns) of two adjacent rows and writes
-//    8 pairs; with a 144-byte row pitch both these writes and the 16-byte
-//    fragment reads are free of bank conflicts.
+//  * The contraction runs over the weight's rows (N), so a matrix-core lane
+//    needs 8 consecutive rows of one column.  The weight tile of a step (64
+//    rows x 128 columns) is dequantized into LDS in its own row order (a
+//    thread: 16 columns of one row, from one 8-byte code load that 8 lanes
+//    make together, written as two 16-byte pieces) and read back transposed
+//    by gfx950's ds_read_b64_tr_b16: in each 16-lane group, result lane i
+//    takes element i % 4 of the 4-element piece addressed by lane
+//    4 e + i / 4 (e the result element; probed on the part).  Two such reads
+//    give a lane its 8 rows.  Rows are 288 bytes apart and the halves of
+//    rows with bit 3 set are swapped, which spreads a read's 4 rows and its
+//    next 16-lane group over distinct banks.  (Transposing on the write
+//    side instead, as pairs of rows, needs row-strided code loads in which
+//    every lane touches its own cache line; that ran at half the speed.)
 //  * dY (the other operand, contiguous along N) is staged per step like the
 //    forward product's activations: 256 rows x 128 bytes with the 16-byte
 //    chunks of a row XOR-swizzled.
-//  * A workgroup of 8 waves computes a 256 x 128 tile of dX; wave w owns
-//    columns 16 w .. 16 w + 15 against all 256 rows (16 accumulators).
-//  * The next step's loads (dY, codes, scales) are issued before the current
-//    step's matrix-core work and written to LDS after it, so HBM/L2 latency
-//    hides behind the MFMAs.
+//  * A workgroup of 8 waves computes a 256 x 128 tile of dX, as 4 (rows) x
+//    2 (columns) waves of 64 x 64: per 32-row half step a wave reads 4
+//    fragments of each operand for 16 MFMAs (with all 256 rows per wave it
+//    read 17 for 16, and the LDS reads, not the matrix cores, set the pace).
+//  * Software pipeline: both LDS tiles are double-buffered (one barrier per
+//    step) and each thread keeps two steps of loads (dY, codes, scales) in
+//    flight in registers, so HBM/L2 latency hides behind two steps of
+//    matrix-core work.
 //  * Tiles are numbered M-block fastest and dealt round-robin to the 8 XCDs,
 //    so each XCD keeps its 256 rows of dY in its own L2.
 #include "q4_common.hpp"
@@ -41,11 +49,12 @@ constexpr int TN = 64;                 // contraction (weight rows) per step
 constexpr int kWaves = 8;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kYRow = TN * 2;          // bytes of one staged dY row
-constexpr int kWPitch = TN * 2 + 16;   // bytes of one staged What^T row
-constexpr int kMF = TM / 16;           // m fragments per wave
+constexpr int kWPitch = TK * 2 + 32;   // bytes of one staged weight row (128 columns)
+constexpr int kKF = 4;                 // k fragments per wave (64 columns)
+constexpr int kWMF = 4;                // m fragments per wave (64 rows)
 
-static_assert(TK == 16 * kWaves, "one 16-column fragment per wave");
-static_assert(TN * TK / 16 == kBlock, "one code dword of two rows per thread");
+static_assert(TK == 2 * 16 * kKF && TM == 4 * 16 * kWMF && kWaves == 8, "2 x 4 waves");
+static_assert(TN * TK / 16 == kBlock, "16 columns of one row per thread");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dx_rsrc(const void *base, int64_t bytes)
 {
@@ -57,6 +66,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dx_rsrc(const void *base, int6
 // Position of 16-byte chunk c of staged dY row r.
 __device__ __forceinline__ int yswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 // One thread's loads of a step: 4 x 16 bytes of dY (row t / 2, chunks
 // 4 (t & 1) .. + 3), and for weight rows 2p, 2p + 1 of the step (p = t % 32)
 // the code dword of columns 8 cq .. 8 cq + 7 (cq = t / 32) with its group's
@@ -64,7 +75,9 @@ __device__ __forceinline__ int yswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // zero-point byte (asym) or run constant (NF4_DQ).
 struct DxLoads {
     u32x4 y[4];
-    uint32_t c[2], s[2], z[2];
+    u32x2 c;
+    uint32_t s, z;
+    int zsh;
 };
 
 struct DxCtx {
@@ -74,8 +87,11 @@ struct DxCtx {
 };
 
 template <int FMT>
-__device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0, int k0)
+__device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0_, int k0)
 {
+    // (the step is wave-uniform; said so, or the compiler may wrap the loads
+    // in a loop over the lanes' values of their scalar offset)
+    const int n0 = __builtin_amdgcn_readfirstlane(n0_);
     const int t = threadIdx.x;
     // dY: elements n0 + 8 chunk .. of row t / 2 of the tile (rows past M and
     // elements past the buffer read zeros; elements past N of a row read the
@@ -86,28 +102,36 @@ __device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0, int
         const int ch = 4 * (t & 1) + i;
         ld.y[i] = __builtin_amdgcn_raw_buffer_load_b128(c.yr, 2 * (yrow * c.N + 8 * ch), 2 * n0, 0);
     }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        // rows past N are clamped to row N: every offset then lies at or
-        // past the end of its view, so codes and scales read zero (no
-        // selects, which the compiler would turn into branches and full
-        // load waits)
-        const int n = min(n0 + 2 * c.p + e, c.N);
-        const int k = k0 + 8 * c.cq;
-        ld.c[e] = __builtin_amdgcn_raw_buffer_load_b32(c.cr, n * (c.K >> 1) + (k >> 1), 0, 0);
-        const int gi = n * c.G + (k >> c.gshift);  // flat group index
-        if constexpr (FMT == Q4_NF4) {
-            ld.s[e] = __builtin_amdgcn_raw_buffer_load_b32(c.sr, 4 * gi, 0, 0);
-        } else if constexpr (FMT == Q4_NF4_DQ) {
-            ld.s[e] = __builtin_amdgcn_raw_buffer_load_b8(c.sr, gi, 0, 0);
-            ld.z[e] = __builtin_amdgcn_raw_buffer_load_b32(c.zr, 4 * (gi >> 8), 0, 0);
-        } else {
-            ld.s[e] = __builtin_amdgcn_raw_buffer_load_b16(c.sr, 2 * gi, 0, 0);
-        }
-        if constexpr (FMT == Q4_INT4_ASYM)
-            ld.z[e] = __builtin_amdgcn_raw_buffer_load_b8(c.zr, gi >> 1, 0, 0) >> (4 * (gi & 1));
+    // weights: row n0 + t / 8 of the step, columns k0 + 16 (t % 8) .. + 15
+    // (8 lanes read a row's 64 bytes of the tile together).  Rows past N
+    // are clamped to row N: every offset then lies at or past the end of its
+    // view, so codes and scales read zero (no selects, which the compiler
+    // would turn into branches and full load waits).
+    const int n = min(n0 + (t >> 3), c.N);
+    const int k = k0 + 16 * (t & 7);
+    ld.c = __builtin_amdgcn_raw_buffer_load_b64(c.cr, n * (c.K >> 1) + (k >> 1), 0, 0);
+    const int gi = n * c.G + (k >> c.gshift);  // flat group index of the 16 columns
+    if constexpr (FMT == Q4_NF4) {
+        ld.s = __builtin_amdgcn_raw_buffer_load_b32(c.sr, 4 * gi, 0, 0);
+    } else if constexpr (FMT == Q4_NF4_DQ) {
+        ld.s = __builtin_amdgcn_raw_buffer_load_b8(c.sr, gi, 0, 0);
+        ld.z = __builtin_amdgcn_raw_buffer_load_b32(c.zr, 4 * (gi >> 8), 0, 0);
+    } else {
+        ld.s = __builtin_amdgcn_raw_buffer_load_b16(c.sr, 2 * gi, 0, 0);
+    }
+    if constexpr (FMT == Q4_INT4_ASYM) {
+        // the byte as loaded (no arithmetic on a load in flight) and the
+        // nibble's position
+        ld.z = __builtin_amdgcn_raw_buffer_load_b8(c.zr, gi >> 1, 0, 0);
+        ld.zsh = 4 * (gi & 1);
     }
 }
+
+// Byte offset in a staged weight tile of element (row nl, column kl): rows
+// of 288 bytes (72 dwords: the 4 rows a transposed read takes fall in
+// distinct banks), the two 128-byte halves swapped on rows with bit 3 set
+// (so that the next group of 8 rows uses the other banks).
+__device__ __forceinline__ int wofs(int nl, int kl) { return nl * kWPitch + ((2 * kl) ^ (((nl >> 3) & 1) << 7)); }
 
 template <int FMT, int ACT>
 __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restrict__ dy, int M,
@@ -117,8 +141,8 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
                                                          int K, int gshift, int mtiles,
                                                          uint16_t *__restrict__ dx)
 {
-    __shared__ __attribute__((aligned(16))) char ys[TM * kYRow];
-    __shared__ __attribute__((aligned(16))) char wt[TK * kWPitch];
+    __shared__ __attribute__((aligned(16))) char ys[2][TM * kYRow];
+    __shared__ __attribute__((aligned(16))) char wt[2][TN * kWPitch];
     __shared__ float2 ptbl[level_fmt(FMT) == Q4_NF4 ? 256 : 1];
 
     const int t = threadIdx.x;
@@ -154,75 +178,166 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
     else
         c.zr = FMT == Q4_INT4_ASYM ? dx_rsrc(zeros, (ngroups + 1) / 2) : c.cr;
 
-    f32x4 acc[kMF];
+    // waves: 2 along k (64 columns each) x 4 along m (64 rows each)
+    const int wk = wave & 1, wm = wave >> 1;
+    f32x4 acc[kKF][kWMF];
 #pragma unroll
-    for (int f = 0; f < kMF; ++f)
-        acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < kKF; ++j)
+#pragma unroll
+        for (int f = 0; f < kWMF; ++f)
+            acc[j][f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    DxLoads ld;
-    dx_load<FMT>(ld, c, 0, k0);
-    for (int n0 = 0; n0 < N; n0 += TN) {
-        __syncthreads();  // the previous step's fragment reads are done (and the table is in)
-        // dY of this step into LDS
-        {
-            const int r = t >> 1;
+    // One round: the products of the step in LDS buffer (ysc, wtc), with the
+    // staging of the next step (register set ld -> buffer (ysn, wtn)) worked
+    // in between the matrix-core instructions, then the loads of a later
+    // step into ld.  Scheduling fences keep that order: the two waves of a
+    // SIMD run in step (one barrier per round), so staging that is not
+    // interleaved leaves the matrix cores idle.
+    auto round = [&](const char *ysc, const char *wtc, char *ysn, char *wtn, DxLoads &ld,
+                     int next_n0) {
+        u32x4 fa[kKF], fb[kWMF];
+        auto reads = [&](int h) {
+            // A operand (8 rows n = 32 h + 8 fq + 0..7 at column k of the
+            // fragment, for lane (k = fi, fq)) by two transposed reads: in
+            // each 16-lane group, result lane i takes element i % 4 of the
+            // 4-element row piece addressed by lane 4 e + i / 4 (e the
+            // result element); so lane s addresses row 8 fq + 4 u + s / 4,
+            // columns 4 (s % 4) .. + 3 of the fragment.
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *(u32x4 *)(ys + r * kYRow + 16 * yswz(r, 4 * (t & 1) + i)) = ld.y[i];
-        }
-        // the weight tile, dequantized and transposed: column 8 cq + i of
-        // rows 2p, 2p + 1 -> the pair at What^T row 8 cq + i, entry p
-        {
-            float v[2][8];
+            for (int j = 0; j < kKF; ++j) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float s, b = 0.0f;
-                if constexpr (FMT == Q4_NF4) {
-                    s = std::bit_cast<float>(ld.s[e]);
-                } else if constexpr (FMT == Q4_NF4_DQ) {
-                    s = keep_f32((float)(ld.s[e] & 0xffu) * std::bit_cast<float>(ld.z[e]));
-                } else {
-                    s = h2f(ld.s[e] & 0xffffu);
-                    b = FMT == Q4_INT4_SYM ? -8.0f * s : -(float)(ld.z[e] & 0xfu) * s;
+                for (int u = 0; u < 2; ++u) {
+                    const int nl = 32 * h + 8 * fq + 4 * u + (fi >> 2);
+                    const int kl = 64 * wk + 16 * j + 4 * (fi & 3);
+                    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)(wtc + wofs(nl, kl)));
+                    fa[j][2 * u] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+                    fa[j][2 * u + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
                 }
-                float2 lp[4];
-                if constexpr (level_fmt(FMT) == Q4_NF4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        lp[i] = ptbl[(ld.c[e] >> (8 * i)) & 0xffu];
-                }
-                dequant8_f32<FMT>(ld.c[e], s, b, lp, v[e]);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *(uint32_t *)(wt + (8 * c.cq + i) * kWPitch + 4 * c.p) = pack2<ACT>(v[0][i], v[1][i]);
+            for (int f = 0; f < kWMF; ++f) {
+                const int r = 64 * wm + 16 * f + fi;
+                fb[f] = *(const u32x4 *)(ysc + r * kYRow + 16 * yswz(r, 4 * h + fq));
+            }
+        };
+        auto mfmas = [&](int j) {
+#pragma unroll
+            for (int f = 0; f < kWMF; ++f)
+                acc[j][f] = mfma<ACT>(fa[j], fb[f], acc[j][f]);
+        };
+        const int yr = t >> 1;
+        // the weight row piece of the next step: 16 columns of row t / 8,
+        // dequantized (pairs along k, as q4_dequantize writes them) and
+        // written as two 16-byte pieces
+        u32x4 wv[2];
+        auto dequant = [&](int e) {
+            float sc, bias = 0.0f;
+            if constexpr (FMT == Q4_NF4) {
+                sc = std::bit_cast<float>(ld.s);
+            } else if constexpr (FMT == Q4_NF4_DQ) {
+                sc = keep_f32((float)(ld.s & 0xffu) * std::bit_cast<float>(ld.z));
+            } else {
+                sc = h2f(ld.s & 0xffffu);
+                bias = FMT == Q4_INT4_SYM ? -8.0f * sc : -(float)((ld.z >> ld.zsh) & 0xfu) * sc;
+            }
+            float2 lp[4];
+            if constexpr (level_fmt(FMT) == Q4_NF4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lp[i] = ptbl[(ld.c[e] >> (8 * i)) & 0xffu];
+            }
+            wv[e] = dequant8<FMT, ACT>(ld.c[e], sc, bias, lp);
+        };
+        auto wwrite = [&](int e) {
+            *(u32x4 *)(wtn + wofs(t >> 3, 16 * (t & 7) + 8 * e)) = wv[e];
+        };
+
+        reads(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kKF; ++j) {
+            mfmas(j);
+            // dY of the next step, one 16-byte piece per group of MFMAs
+            *(u32x4 *)(ysn + yr * kYRow + 16 * yswz(yr, 4 * (t & 1) + j)) = ld.y[j];
+            __builtin_amdgcn_sched_barrier(0);
         }
+        reads(1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        dequant(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        dequant(1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(2);
+        wwrite(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(3);
+        wwrite(1);
+        __builtin_amdgcn_sched_barrier(0);
+        dx_load<FMT>(ld, c, next_n0, k0);
         __syncthreads();
-        // the next step's loads, in flight during this step's products
-        if (n0 + TN < N)
-            dx_load<FMT>(ld, c, n0 + TN, k0);
-        // dX[16 f + fi][16 wave + 4 fq + v] += sum over the step's 64 rows
+    };
+
+    // Software pipeline: LDS double-buffered (one barrier per step), and two
+    // steps of loads in flight in registers.  On entry to the round of step
+    // s, buffer s & 1 holds step s, one register set step s + 1 and the
+    // other step s + 2.  Loads of steps past the end read zeros (rows
+    // clamped) or unused data; the buffers they fill are never computed.
+    const int nsteps = (N + TN - 1) / TN;
+    DxLoads la, lb;
+    dx_load<FMT>(la, c, 0, k0);
+    dx_load<FMT>(lb, c, TN, k0);
+    __syncthreads();  // the level-pair table
+    {
+        // step 0 into buffer 0 (no products yet)
+        const int yr = t >> 1;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4 a = *(const u32x4 *)(wt + (16 * wave + fi) * kWPitch + 64 * h + 16 * fq);
+        for (int i = 0; i < 4; ++i)
+            *(u32x4 *)(ys[0] + yr * kYRow + 16 * yswz(yr, 4 * (t & 1) + i)) = la.y[i];
+        float sc, bias = 0.0f;
+        if constexpr (FMT == Q4_NF4) {
+            sc = std::bit_cast<float>(la.s);
+        } else if constexpr (FMT == Q4_NF4_DQ) {
+            sc = keep_f32((float)(la.s & 0xffu) * std::bit_cast<float>(la.z));
+        } else {
+            sc = h2f(la.s & 0xffffu);
+            bias = FMT == Q4_INT4_SYM ? -8.0f * sc : -(float)((la.z >> la.zsh) & 0xfu) * sc;
+        }
 #pragma unroll
-            for (int f = 0; f < kMF; ++f) {
-                const int r = 16 * f + fi;
-                const u32x4 bv = *(const u32x4 *)(ys + r * kYRow + 16 * yswz(r, 4 * h + fq));
-                acc[f] = mfma<ACT>(a, bv, acc[f]);
+        for (int e = 0; e < 2; ++e) {
+            float2 lp[4];
+            if constexpr (level_fmt(FMT) == Q4_NF4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lp[i] = ptbl[(la.c[e] >> (8 * i)) & 0xffu];
             }
+            *(u32x4 *)(wt[0] + wofs(t >> 3, 16 * (t & 7) + 8 * e)) = dequant8<FMT, ACT>(la.c[e], sc, bias, lp);
         }
     }
+    dx_load<FMT>(la, c, 2 * TN, k0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+        round(ys[0], wt[0], ys[1], wt[1], lb, (st + 3) * TN);  // step st; stages st + 1
+        if (st + 1 >= nsteps)
+            break;
+        round(ys[1], wt[1], ys[0], wt[0], la, (st + 4) * TN);  // step st + 1; stages st + 2
+    }
 
-    // lane (fi, fq) of fragment f holds dX[m0 + 16 f + fi][k0 + 16 wave + 4 fq + v]
-    const int k = k0 + 16 * wave + 4 * fq;
-    if (k < K) {
+    // lane (fi, fq) of fragment (j, f) holds
+    // dX[m0 + 64 wm + 16 f + fi][k0 + 64 wk + 16 j + 4 fq + v]
 #pragma unroll
-        for (int f = 0; f < kMF; ++f) {
-            const int m = m0 + 16 * f + fi;
-            if (m < M)
-                *(u32x2 *)(dx + (int64_t)m * K + k) =
-                    u32x2{pack2<ACT>(acc[f][0], acc[f][1]), pack2<ACT>(acc[f][2], acc[f][3])};
+    for (int j = 0; j < kKF; ++j) {
+        const int k = k0 + 64 * wk + 16 * j + 4 * fq;
+        if (k < K) {
+#pragma unroll
+            for (int f = 0; f < kWMF; ++f) {
+                const int m = m0 + 64 * wm + 16 * f + fi;
+                if (m < M)
+                    *(u32x2 *)(dx + (int64_t)m * K + k) = u32x2{
+                        pack2<ACT>(acc[j][f][0], acc[j][f][1]), pack2<ACT>(acc[j][f][2], acc[j][f][3])};
+            }
         }
     }
 }
