@@ -11,10 +11,14 @@
 // v_mfma_f32_16x16x32 instead of the vector ALUs.
 //
 // gfx950 mapping:
-//  * A workgroup owns 16 weight rows (one MFMA operand of 16 rows) and all
-//    M <= 16 activation rows; its 8 waves split K into steps of 128,
-//    interleaved (wave w takes steps w, w + 8, ...), so even a 4096-row
-//    matrix gives 2048 streaming waves.
+//  * A workgroup owns RB blocks of 16 weight rows (one MFMA operand each)
+//    and all M <= 16 activation rows; its 8 waves split K into steps of
+//    128, interleaved (wave w takes steps w, w + 8, ...).  A step's x
+//    fragment serves all RB blocks, so each workgroup reads x once for RB
+//    blocks; RB (1, 2 or 4) is the largest that still gives every compute
+//    unit a workgroup.  (Without x loads at all, a timing-only variant ran
+//    twice as fast at M = 16; halving them gained only 6 %: what the x loads
+//    cost is mostly their latency in a pipeline of few steps per wave.)
 //  * Lane (r, q) = (lane % 16, lane / 16) loads 16 bytes of codes: 32
 //    weights of row r at k = k0 + 32 q.  Dword d of them is the lane's share
 //    of MFMA d of the step, which therefore contracts over k0 + 32 q + 8 d
@@ -49,17 +53,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void *base, int6
                                              0x00020000);
 }
 
-// One step's operands for a lane: 32 codes, their group's scale (and asym
-// zero-point), and 32 activations of one x row.
-template <int FMT>
+// One step's operands for a lane: for each of the RB row blocks, 32 codes
+// and their group's scale (and asym zero-point, or NF4_DQ run constant);
+// and 32 activations of one x row, shared by the blocks.
+template <int FMT, int RB>
 struct SkStep {
-    u32x4 cw;
-    uint32_t sraw;
-    uint32_t zraw;
+    u32x4 cw[RB];
+    uint32_t sraw[RB];
+    uint32_t zraw[RB];
+    int zsh[RB];
     u32x4 xv[4];
 };
 
-template <int FMT, int ACT>
+template <int FMT, int ACT, int RB>
 __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K, int gshift,
@@ -67,12 +73,12 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
 {
     constexpr int LF = level_fmt(FMT);
     __shared__ float2 ptbl[LF == Q4_NF4 ? 256 : 1];
-    __shared__ f32x4 part[kSkWaves][64];
+    __shared__ f32x4 part[kSkWaves][RB][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * RB;
     const int G = K >> gshift;
     const int row_bytes = K >> 1;
     constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
@@ -82,18 +88,18 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
             ptbl[threadIdx.x] = float2{kNF4[threadIdx.x & 15], kNF4[threadIdx.x >> 4]};
     }
 
-    // views: this block's 16 weight rows (rows past N read zeros) and the M
-    // activation rows
-    const int nrows = N - n0 < 16 ? N - n0 : 16;
+    // views: this workgroup's 16 RB weight rows (rows past N read zeros) and
+    // the M activation rows
+    const int nrows = N - n0 < 16 * RB ? N - n0 : 16 * RB;
     const __amdgpu_buffer_rsrc_t cr = sk_rsrc(codes + (int64_t)n0 * row_bytes, (int64_t)nrows * row_bytes);
     const __amdgpu_buffer_rsrc_t sr =
         sk_rsrc((const char *)scales + (int64_t)n0 * G * ss, (int64_t)nrows * G * ss);
-    const int64_t zg0 = (int64_t)n0 * G;  // flat group index of the block's first group
+    const int64_t zg0 = (int64_t)n0 * G;  // flat group index of the first row's first group
     __amdgpu_buffer_rsrc_t zr = sr;
     if constexpr (FMT == Q4_INT4_ASYM)
         zr = sk_rsrc(zeros + (zg0 >> 1), (((int64_t)nrows * G + (zg0 & 1)) + 1) / 2);
-    // double-quantized absmax: the runs' binary32 constants for the block's
-    // groups (zr then starts at the run holding the block's first group)
+    // double-quantized absmax: the runs' binary32 constants for the rows'
+    // groups (zr then starts at the run holding the first group)
     if constexpr (FMT == Q4_NF4_DQ) {
         const float *s2 = (const float *)((const char *)scales + dq_s2_offset((int64_t)N * G));
         const int64_t r0 = zg0 / kDqRun, r1 = (zg0 + (int64_t)nrows * G - 1) / kDqRun;
@@ -102,26 +108,34 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const __amdgpu_buffer_rsrc_t xr = sk_rsrc(x, (int64_t)M * K * 2);
 
     const int nsteps = (K + kSkStep - 1) / kSkStep;
-    auto load = [&](SkStep<FMT> &st, int step) {
+    auto load = [&](SkStep<FMT, RB> &st, int step) {
         const int k = step * kSkStep + 32 * q;  // the lane's first k
         const bool in = step < nsteps && k < K;
-        st.cw = __builtin_amdgcn_raw_buffer_load_b128(cr, in ? r * row_bytes + (k >> 1) : -16, 0, 0);
-        const int gi = r * G + (k >> gshift);  // group within the block
-        if constexpr (FMT == Q4_NF4)
-            st.sraw = __builtin_amdgcn_raw_buffer_load_b32(sr, in ? 4 * gi : -16, 0, 0);
-        else if constexpr (FMT == Q4_NF4_DQ)
-            st.sraw = __builtin_amdgcn_raw_buffer_load_b8(sr, in ? gi : -16, 0, 0);
-        else
-            st.sraw = __builtin_amdgcn_raw_buffer_load_b16(sr, in ? 2 * gi : -16, 0, 0);
-        if constexpr (FMT == Q4_INT4_ASYM) {
-            const int gz = (int)(zg0 & 1) + gi;
-            st.zraw = __builtin_amdgcn_raw_buffer_load_b8(zr, in ? gz >> 1 : -16, 0, 0) >>
-                      (4 * (gz & 1));
-        } else if constexpr (FMT == Q4_NF4_DQ) {
-            const int gr = (int)(zg0 % kDqRun) + gi;  // group index from the first run's start
-            st.zraw = __builtin_amdgcn_raw_buffer_load_b32(zr, in ? 4 * (gr / kDqRun) : -16, 0, 0);
-        } else {
-            st.zraw = 0;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int rr = 16 * b + r;  // the lane's weight row in the workgroup
+            st.cw[b] = __builtin_amdgcn_raw_buffer_load_b128(cr, in ? rr * row_bytes + (k >> 1) : -16,
+                                                             0, 0);
+            const int gi = rr * G + (k >> gshift);  // group within the workgroup's rows
+            if constexpr (FMT == Q4_NF4)
+                st.sraw[b] = __builtin_amdgcn_raw_buffer_load_b32(sr, in ? 4 * gi : -16, 0, 0);
+            else if constexpr (FMT == Q4_NF4_DQ)
+                st.sraw[b] = __builtin_amdgcn_raw_buffer_load_b8(sr, in ? gi : -16, 0, 0);
+            else
+                st.sraw[b] = __builtin_amdgcn_raw_buffer_load_b16(sr, in ? 2 * gi : -16, 0, 0);
+            if constexpr (FMT == Q4_INT4_ASYM) {
+                // the byte as loaded (no arithmetic on a load in flight) and
+                // the nibble's position
+                const int gz = (int)(zg0 & 1) + gi;
+                st.zraw[b] = __builtin_amdgcn_raw_buffer_load_b8(zr, in ? gz >> 1 : -16, 0, 0);
+                st.zsh[b] = 4 * (gz & 1);
+            } else if constexpr (FMT == Q4_NF4_DQ) {
+                const int gr = (int)(zg0 % kDqRun) + gi;  // group index from the first run's start
+                st.zraw[b] =
+                    __builtin_amdgcn_raw_buffer_load_b32(zr, in ? 4 * (gr / kDqRun) : -16, 0, 0);
+            } else {
+                st.zraw[b] = 0;
+            }
         }
         const bool xin = in && r < M;
 #pragma unroll
@@ -131,60 +145,68 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     };
 
     // the wave's steps: wave, wave + 8, ...
-    SkStep<FMT> ring[kSkRing];
+    SkStep<FMT, RB> ring[kSkRing];
 #pragma unroll
     for (int i = 0; i < kSkRing; ++i)
         load(ring[i], wave + kSkWaves * i);
     __syncthreads();  // the level-pair table
 
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+        acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int step = wave; step < nsteps; step += kSkWaves * kSkRing) {
 #pragma unroll
         for (int i = 0; i < kSkRing; ++i) {
-            const int cs = step + kSkWaves * i;
-            SkStep<FMT> &st = ring[i];
+            SkStep<FMT, RB> &st = ring[i];
             // every path computes (a step past the end has zero codes,
             // scales and x), so the load waits stay partial
-            float s, b;
-            if constexpr (FMT == Q4_NF4) {
-                s = std::bit_cast<float>(st.sraw);
-                b = 0.0f;
-            } else if constexpr (FMT == Q4_NF4_DQ) {  // c' = qc * s2, one product
-                s = keep_f32((float)st.sraw * std::bit_cast<float>(st.zraw));
-                b = 0.0f;
-            } else {
-                s = h2f(st.sraw & 0xffffu);
-                b = FMT == Q4_INT4_SYM ? -8.0f * s : -(float)(st.zraw & 0xfu) * s;
-            }
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float2 lp[4];
-                if constexpr (LF == Q4_NF4) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        lp[e] = ptbl[(st.cw[d] >> (8 * e)) & 0xffu];
+            for (int b = 0; b < RB; ++b) {
+                float s, bias;
+                if constexpr (FMT == Q4_NF4) {
+                    s = std::bit_cast<float>(st.sraw[b]);
+                    bias = 0.0f;
+                } else if constexpr (FMT == Q4_NF4_DQ) {  // c' = qc * s2, one product
+                    s = keep_f32((float)st.sraw[b] * std::bit_cast<float>(st.zraw[b]));
+                    bias = 0.0f;
+                } else {
+                    s = h2f(st.sraw[b] & 0xffffu);
+                    bias = FMT == Q4_INT4_SYM ? -8.0f * s
+                                              : -(float)((st.zraw[b] >> st.zsh[b]) & 0xfu) * s;
                 }
-                const u32x4 wf = dequant8<FMT, ACT>(st.cw[d], s, b, lp);
-                acc = mfma<ACT>(wf, st.xv[d], acc);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    float2 lp[4];
+                    if constexpr (LF == Q4_NF4) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            lp[e] = ptbl[(st.cw[b][d] >> (8 * e)) & 0xffu];
+                    }
+                    const u32x4 wf = dequant8<FMT, ACT>(st.cw[b][d], s, bias, lp);
+                    acc[b] = mfma<ACT>(wf, st.xv[d], acc[b]);
+                }
             }
-            (void)cs;
             load(st, step + kSkWaves * (i + kSkRing));
         }
     }
 
-    // sum the 8 partial tiles in wave order; lane l holds rows 4 q + v of
-    // the block against activation row r
-    part[wave][lane] = acc;
+    // sum the 8 partial tiles of each block in wave order; lane l holds rows
+    // 4 q + v of the block against activation row r
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+        part[wave][b][lane] = acc[b];
     __syncthreads();
-    if (wave == 0) {
-        f32x4 t = part[0][lane];
+    if (wave < RB) {
+        const int b = wave;
+        f32x4 t = part[0][b][lane];
 #pragma unroll
         for (int w = 1; w < kSkWaves; ++w) {
-            const f32x4 u = part[w][lane];
+            const f32x4 u = part[w][b][lane];
             t = f32x4{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
         }
         const int m = r;
-        const int n = n0 + 4 * q;
+        const int n = n0 + 16 * b + 4 * q;
         if (m < M) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -196,21 +218,37 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     }
 }
 
+template <int FMT, int RB>
+hipError_t launch_sk_rb(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
+                        const void *scales, const uint8_t *zeros, int64_t N, int64_t K, int gshift,
+                        void *y, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)((N + 16 * RB - 1) / (16 * RB));
+    if (act_t == Q4_BF16)
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_BF16, RB>), dim3(blocks), dim3(kSkBlock), 0, s,
+                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
+                           (uint16_t *)y);
+    else
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_F16, RB>), dim3(blocks), dim3(kSkBlock), 0, s,
+                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
+                           (uint16_t *)y);
+    return hipGetLastError();
+}
+
+// Row blocks per workgroup: as many (up to 4) as keep at least one
+// workgroup per compute unit, so that x is read once for several blocks.
 template <int FMT>
 hipError_t launch_sk_fmt(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
                          const void *scales, const uint8_t *zeros, int64_t N, int64_t K,
                          int gshift, void *y, hipStream_t s)
 {
-    const unsigned blocks = (unsigned)((N + 15) / 16);
-    if (act_t == Q4_BF16)
-        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_BF16>), dim3(blocks), dim3(kSkBlock), 0, s,
-                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
-                           (uint16_t *)y);
-    else
-        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_F16>), dim3(blocks), dim3(kSkBlock), 0, s,
-                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
-                           (uint16_t *)y);
-    return hipGetLastError();
+    const int64_t nb = (N + 15) / 16;
+    const int64_t cus = device_cu_count();
+    if (nb >= 4 * cus)
+        return launch_sk_rb<FMT, 4>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
+    if (nb >= 2 * cus)
+        return launch_sk_rb<FMT, 2>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
+    return launch_sk_rb<FMT, 1>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
 }
 
 }  // namespace
