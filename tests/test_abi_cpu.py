@@ -189,6 +189,8 @@ def test_gemv_task_layout():
     (dict(zeros=A), q4.EINVAL),
     (dict(flags=2), q4.EINVAL),
     (dict(K=16384 + 64), q4.EUNSUPPORTED),       # x no longer fits the LDS buffers
+    (dict(N=262144, K=16384), q4.EUNSUPPORTED),   # codes 2 GiB: past Q4_GEMV_CHAIN_MAX_CODES
+    (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),
 ])
 def test_chain_rejects(kw, status):
     assert call_chain(**kw) == status
