@@ -126,3 +126,37 @@ def test_c5_token_launch_shapes(name, parts, K):
     ys = y[:, torch.from_numpy(rows).to(y.device)]
     yr, ad = oracle.matmul(q4.NF4, 64, q4.BF16, x_bits, oc, os_, None, rows.size, K)
     assert_product_ok(ys, yr, ad, tag=f"c5 {name}")
+
+
+def test_c5_token_shapes_double_quantized_chain():
+    """The decode token's four launch shapes with double-quantized absmax,
+    run as one chained launch (as the benchmark's dq leg runs them).  The
+    second-level runs cross rows, so the oracle quantizes each whole matrix;
+    code bytes and 8-bit absmax codes are compared on sampled rows, the run
+    constants in full, and the products on sampled rows."""
+    shapes = [("qkv", [(4096, 0), (4096, 1), (4096, 2)], 4096), ("o", [(4096, 3)], 4096),
+              ("gate_up", [(11008, 4), (11008, 5)], 4096), ("down", [(4096, 6)], 11008)]
+    tasks, refs = [], []
+    for name, parts, K in shapes:
+        print(f"dq c5 {name}", flush=True)
+        w = _layer0(parts, K)
+        N = w.shape[0]
+        q = q4.quantize(dev16(w), q4.NF4_DQ, 64)
+        oc, os_, _ = oracle.quantize(q4.NF4_DQ, 64, w)
+        torch.cuda.synchronize()
+        rows = _sample_rows(N, 11 * N + K)
+        G = K // 64
+        gq, gs2 = (t.cpu().numpy() for t in q4.dq_parts(q))
+        oq, os2 = oracle.dq_split(os_, N * G)
+        assert np.array_equal(q.codes.cpu().numpy()[rows], oc[rows]), f"{name}: codes differ"
+        assert np.array_equal(gq[rows], oq.reshape(N, G)[rows]), f"{name}: absmax codes differ"
+        assert np.array_equal(gs2.view(np.uint32), os2.view(np.uint32)), f"{name}: run constants"
+        x_bits = synth.act_bits(1, K, 5900 if K == 4096 else 5901, synth.BF16)
+        tasks.append((dev16(x_bits, q4.BF16), q, None, q4.TASK_NO_WAIT))
+        refs.append((name, rows, oracle.matmul(q4.NF4_DQ, 64, q4.BF16, x_bits, oc, os_, None, N,
+                                               K, rows=rows)))
+    outs = q4.gemv_chain(tasks)
+    torch.cuda.synchronize()
+    for y, (name, rows, (yr, ad)) in zip(outs, refs):
+        ys = y[:, torch.from_numpy(rows).to(y.device)]
+        assert_product_ok(ys, yr, ad, tag=f"dq c5 {name}")
