@@ -666,16 +666,19 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 // The weights never depend on earlier tasks, so each compute wave's ring of
 // in-flight weight loads runs on across task boundaries.  Only x may depend
 // on earlier tasks.  A workgroup is 15 compute waves and one loader wave.
-// x sits in LDS, double-buffered, as loaded (linear); each lane of a compute
-// wave converts its own chunks in registers, as the single-product kernels
-// do when staging.  The loader copies x of task t in by LDS-DMA once every
-// compute wave has entered task t - 1 (so the buffer's previous task is
-// done), waits for it (it has no weight loads to drain) and publishes it; a
-// compute wave entering task t waits only for that.  For a task that reads
-// earlier outputs the loader first waits until every compute wave has
-// finished the earlier tasks, then for the whole grid (a grid barrier
-// between loader waves).  The compute waves never wait for each other.  The
-// table is filled once per launch.
+// x sits in LDS in 8 slots of one stage each (8 KB); task t's stages take
+// consecutive slots from slot base_t on (mod 8), tasks in turn, so a slot is
+// reused only by a task at least two later.  The loader copies x of task t
+// once every compute wave has entered the task after the last one that used
+// those slots (the gate, computed on the host) and publishes it; a compute
+// wave entering task t waits only for that.  So waves may drift several
+// tasks apart: with a double buffer they could not get more than one task
+// ahead of the slowest, and a task of about one row per wave ran at the
+// pace of the waves that got two.  For a task that reads earlier outputs
+// the loader first waits until every compute wave has finished the earlier
+// tasks, then for the whole grid (a grid barrier between loader waves).
+// The compute waves never wait for each other.  The table is filled once
+// per launch.
 struct ChainTask {
     const uint16_t *x;
     const uint8_t *codes;
@@ -683,8 +686,15 @@ struct ChainTask {
     const uint8_t *zeros;
     uint16_t *y;
     int N, K;
-    int wait;  // 1: wait for every earlier task before reading x
+    // bit 0: wait for every earlier task before reading x; bits 1-3: the
+    // first x slot; bits 8-15: the gate (every compute wave must have
+    // entered that task before x is copied)
+    int ctl;
 };
+__device__ __forceinline__ bool ctl_wait(int ctl) { return ctl & 1; }
+__device__ __forceinline__ int ctl_base(int ctl) { return (ctl >> 1) & 7; }
+__device__ __forceinline__ int ctl_gate(int ctl) { return (ctl >> 8) & 0xff; }
+constexpr int kChainSlots = 8;
 constexpr int kChainMax = Q4_GEMV_CHAIN_MAX;
 struct ChainArgs {
     ChainTask t[kChainMax];
@@ -695,18 +705,19 @@ struct ChainArgs {
     uint32_t *sync;
 };
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a second)
-constexpr int kChainMaxK = 16384;
-constexpr int kChainLinBytes = 2 * kChainMaxK;  // one buffer of x as loaded
+constexpr int kChainMaxK = 16384;  // 4 stages: a task and the next fit the 8 slots
 
 // A wave's position in the chain: task, row and stage along K; whether the
-// stage is the row's last, and where the row's output goes.
+// stage is the row's last, where the row's output goes and the task's first
+// x slot.
 struct CPos {
     int t, row, s;
     bool last;
     uint16_t *yp;
+    int xbase;
 };
 
-__device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
+__host__ __device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
 
 // The views of one task for the chained kernel: whole arrays (each under
 // 2 GiB, checked on the host), with a row's and a stage's place added as a
@@ -717,7 +728,7 @@ struct TaskViews {
     __amdgpu_buffer_rsrc_t codes, scales, zeros;
     const float *s2;  // double quantization: the second-level constants
     uint16_t *y;
-    int N, S, C, row_bytes, G;
+    int N, S, C, row_bytes, G, xbase;
 };
 constexpr uint32_t kChainOob = 0x80000000u;
 
@@ -736,6 +747,7 @@ __device__ __forceinline__ TaskViews task_views(const ChainTask &T, int gshift)
     v.zeros = FMT == Q4_INT4_ASYM ? make_rsrc(T.zeros, ((int64_t)v.N * v.G + 1) / 2) : v.codes;
     v.s2 = (const float *)T.zeros;
     v.y = T.y;
+    v.xbase = ctl_base(T.ctl);
     return v;
 }
 
@@ -798,78 +810,132 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-#ifndef CHAIN_XB
-#define CHAIN_XB 2
-#endif
-
-// x of a chained task in LDS: piece-major within each stage (stage s, piece
-// j of its local chunk c at 16-byte index 512 s + 128 j + c), so that the 16
-// lanes of a read pass take 256 consecutive bytes (no bank conflicts).
-__device__ __forceinline__ int chain_x_index(int s, int j, int c) { return 512 * s + 128 * j + c; }
+// x of a chained task in LDS: stage s in slot (base + s) mod 8, piece-major
+// within the stage (piece j of its local chunk c at 16-byte index
+// 128 j + c of the slot), so that the 16 lanes of a read pass take 256
+// consecutive bytes (no bank conflicts); the inverse scales of stage s at
+// float index 128 slot + c.
+__device__ __forceinline__ int chain_slot(int base, int s) { return (base + s) & (kChainSlots - 1); }
+__device__ __forceinline__ int chain_x_index(int slot, int j, int c) { return 512 * slot + 128 * j + c; }
 
 // A lane's x slice for stage s of a row: chunks l and 64 + l of the stage
 // (the stored rows are zero past K up to whole stages), with the inverse
 // scales of their conversion.
 __device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2], const u32x4 *xb,
-                                              const float *inv, int s, int lane)
+                                              const float *inv, int base, int s, int lane)
 {
+    const int slot = chain_slot(base, s);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            xreg[4 * h + j] = xb[chain_x_index(s, j, 64 * h + lane)];
-        xinv[h] = inv[stage_chunk(s, lane, h)];
+            xreg[4 * h + j] = xb[chain_x_index(slot, j, 64 * h + lane)];
+        xinv[h] = inv[kStageChunks * slot + 64 * h + lane];
     }
 }
 
-// The loader's copy of x[0, K) of a task into LDS, zero-padded to whole
-// stages, CHAIN_XB chunks of 32 values per lane at a time: converted where the arithmetic
-// uses fp16 for bf16 activations (per 32-value chunk, max |x| scaled into
-// [2^14, 2^15) by a power of two: the staged single-product conversion),
-// written piece-major; inv receives the chunks' inverse scales (1 when
-// nothing is converted).
-template <int FMT, int ACT>
-__device__ __forceinline__ void chain_load_x(const ChainTask &T, u32x4 *xb, float *inv, int lane)
+// A task's descriptor from the table's copy in LDS, in scalar registers.
+__device__ __forceinline__ ChainTask lds_task(const ChainTask *tasks, int t)
 {
-    using F = Cfg<FMT, ACT, X_LDS>;
-    constexpr int kB = CHAIN_XB;  // chunks per lane per batch
-    // chunks up to the end of the last stage: past K the loads return zeros
-    const int C = chain_stages(T.K) * kStageChunks;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
-    for (int c0 = 0; c0 < C; c0 += 64 * kB) {
-        u32x4 v[kB][4];
+    constexpr int W = sizeof(ChainTask) / 4;
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(tasks + t);
+    uint32_t w[W];
 #pragma unroll
-        for (int i = 0; i < kB; ++i)
+    for (int i = 0; i < W; ++i)
+        w[i] = __builtin_amdgcn_readfirstlane(p[i]);
+    ChainTask T;
+    __builtin_memcpy(&T, w, sizeof(T));
+    return T;
+}
+
+// x DMA instructions per stage: 2 halves of 64 chunks, 4 pieces each.
+constexpr int kChainDmaPerStage = 8;
+// x DMA instructions of later tasks the loader keeps in flight at most (a
+// multiple of kChainDmaPerStage, within the vector-memory counter's range).
+constexpr int kChainDmaAhead = 40;
+
+// The loader's copy of x[0, K) of a task into the task's slots, by the
+// buffer unit straight into LDS (no registers, so the loader can have
+// several tasks in flight): per stage, half and piece, one 16-byte load per
+// lane, lane l's piece j of chunk c0 + l landing at 16-byte index
+// 128 j + c0 + l of the slot, the piece-major order the compute waves read.
+// Chunks past K read zeros: the stored rows are padded to whole stages.
+__device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int lane)
+{
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
+    const int S = chain_stages(T.K);
+    const int base = ctl_base(T.ctl);
+    for (int s = 0; s < S; ++s) {
+        const int slot = chain_slot(base, s);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                v[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, 64 * (c0 + 64 * i + lane) + 16 * j, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (__attribute__((address_space(3))) void *)(xb + chain_x_index(slot, j, 64 * h)),
+                    16, 64 * lane, 64 * (kStageChunks * s + 64 * h) + 16 * j, 0, 0);
+    }
+}
+
+// Once a task's x is in its slots: converted in place where the arithmetic
+// uses fp16 for bf16 activations (per 32-value chunk, max |x| scaled into
+// [2^14, 2^15) by a power of two: the staged single-product conversion);
+// inv receives the chunks' inverse scales (1 when nothing is converted).
+template <int FMT, int ACT>
+__device__ __forceinline__ void chain_convert_x(const ChainTask &T, u32x4 *xb, float *inv, int lane)
+{
+    using F = Cfg<FMT, ACT, X_LDS>;
+    const int S = chain_stages(T.K);
+    const int base = ctl_base(T.ctl);
+    for (int s = 0; s < S; ++s) {
+        const int slot = chain_slot(base, s);
 #pragma unroll
-        for (int i = 0; i < kB; ++i) {
-            const int c = c0 + 64 * i + lane;
+        for (int h = 0; h < 2; ++h) {
+            const int c = 64 * h + lane;
             float iv = 1.0f;
             if constexpr (F::conv_x) {
+                u32x4 v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = xb[chain_x_index(slot, j, c)];
                 float mx = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        mx = fmaxf(mx, bf2_absmax(v[i][j][k]));
+                        mx = fmaxf(mx, bf2_absmax(v[j][k]));
                 float f;
                 x_scale(mx, f, iv);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        v[i][j][k] = bf2_to_h2(v[i][j][k], f);
+                        v[j][k] = bf2_to_h2(v[j][k], f);
+                    xb[chain_x_index(slot, j, c)] = v[j];
+                }
             }
-            if (c < C) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xb[chain_x_index(c >> 7, j, c & 127)] = v[i][j];
-                inv[c] = iv;
-            }
+            inv[kStageChunks * slot + c] = iv;
         }
     }
+}
+
+// Waits until at most n vector-memory instructions (a multiple of
+// kChainDmaPerStage, at most kChainDmaAhead) are in flight.
+__device__ __forceinline__ void wait_vm_upto(int n)
+{
+    static_assert(kChainDmaAhead == 40 && kChainDmaPerStage == 8, "bins below");
+    if (n >= 40)
+        wait_vm<40>();
+    else if (n >= 32)
+        wait_vm<32>();
+    else if (n >= 24)
+        wait_vm<24>();
+    else if (n >= 16)
+        wait_vm<16>();
+    else if (n >= 8)
+        wait_vm<8>();
+    else
+        wait_vm<0>();
 }
 
 constexpr int kChainCompute = 15;  // compute waves per workgroup (wave 15 loads x)
@@ -887,10 +953,11 @@ void gemv_chain_kernel(const ChainArgs a)
     // address is the v_perm result itself.
     struct Lds {
         uint32_t tbl[kTableDwords];
-        u32x4 xb[2][kChainLinBytes / 16];
-        float xinv[2][kChainMaxK / 32];
-        int entered[2];  // compute waves that entered tasks of each parity (cumulative)
-        int ready[2];    // the task whose x lin[parity] holds
+        u32x4 xb[kChainSlots * 512];
+        float xinv[kChainSlots * kStageChunks];
+        int entered[kChainMax];  // compute waves that entered each task
+        int ready[kChainMax];    // 1 once x of the task is in its slots
+        ChainTask tasks[kChainMax];
     };
     __shared__ Lds lds;
     uint32_t *const tbl = lds.tbl;
@@ -905,8 +972,8 @@ void gemv_chain_kernel(const ChainArgs a)
     const int nt = a.ntasks;
     // every compute wave has entered task t
     auto all_entered = [&](int t) {
-        return __hip_atomic_load(&entered[t & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
-               kChainCompute * (t / 2 + 1);
+        return __hip_atomic_load(&entered[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
+               kChainCompute;
     };
     auto fail = [&]() { __hip_atomic_store(&a.sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 
@@ -942,58 +1009,101 @@ void gemv_chain_kernel(const ChainArgs a)
             ((u32x4 *)tbl)[piece] = u32x4{v, v, v, v};
         }
     }
+    // the task table into LDS, read there at every task switch: through the
+    // scalar cache, a miss would stall the wave (and the loads of its next
+    // rows) for a loaded memory system's latency once per task
+    {
+        constexpr int W = sizeof(ChainTask) / 4;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(&a.t[0]);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(lds.tasks);
+        static_assert(kChainMax * W <= 1024, "one word per thread");
+        if ((int)threadIdx.x < nt * W)
+            dst[threadIdx.x] = src[threadIdx.x];
+    }
+    __syncthreads();
+    auto task = [&](int t) { return lds_task(lds.tasks, t); };
 
     if (wave == kChainCompute) {
         // ---------------------------------------------------------- loader
-        auto copy_x = [&](int t) {
-            chain_load_x<FMT, ACT>(a.t[t], xb[t & 1], xinv_lds[t & 1], lane);
+        // x goes in by DMA as early as the slots allow: a later task's as
+        // soon as its gate is open (unless it reads earlier outputs), up to
+        // kChainDmaAhead instructions ahead; the current task's is then
+        // awaited, converted and published.
+        int issued = 0;  // tasks whose x DMA is issued (in order)
+        int ahead = 0;   // DMA instructions in flight for tasks after the current one
+        auto dma_count = [&](const ChainTask &T) { return kChainDmaPerStage * chain_stages(T.K); };
+        auto issue_ahead = [&]() {
+            while (issued < nt) {
+                const ChainTask T = task(issued);
+                const int n = dma_count(T);
+                if ((DEP && ctl_wait(T.ctl)) || ahead + n > kChainDmaAhead || !all_entered(ctl_gate(T.ctl)))
+                    break;
+                chain_dma_x(T, xb, lane);
+                ahead += n;
+                ++issued;
+            }
+        };
+        auto publish = [&](int t) {
+            wait_vm_upto(ahead);  // task t's DMA is done (they complete in order)
+            chain_convert_x<FMT, ACT>(task(t), xb, xinv_lds, lane);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): x is in LDS
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __hip_atomic_store(&ready[t & 1], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&ready[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
-        if (lane == 0) {
-            entered[0] = kChainCompute;  // task 0 is entered by every compute wave in the prologue
-            entered[1] = 0;
-            ready[0] = ready[1] = -1;
-        }
-        copy_x(0);
+        // task 0 is entered by every compute wave in the prologue
+        entered[lane] = lane == 0 ? kChainCompute : 0;
+        ready[lane] = 0;
+        chain_dma_x(task(0), xb, lane);
+        issued = 1;
+        issue_ahead();
+        publish(0);
         __syncthreads();  // the table, the counters and x of task 0
         int nbar = 0;
         for (int t = 1; t < nt; ++t) {
-            // lin[t & 1] held x of task t - 2: wait until every compute wave
-            // has entered t - 1; a task that reads earlier outputs waits
-            // until they have finished t - 1 (entered t, stores complete)
-            const bool wait = DEP && a.t[t].wait;
-            const int need = wait ? t : t - 1;
-            uint32_t spins = 0;
-            while (!all_entered(need)) {
-                if (++spins == kSpinLimit) {
-                    fail();
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (wait) {
-                // grid barrier between the loaders: this workgroup's
-                // outputs are released with the arrival, the others'
-                // acquired after it
-                ++nbar;
-                if (lane == 0) {
-                    __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                    const uint32_t target = (uint32_t)nbar * gridDim.x;
-                    uint32_t gspins = 0;
-                    while (__hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                           target) {
-                        if (++gspins == kSpinLimit) {
-                            fail();
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
+            const ChainTask T = task(t);
+            if (issued > t) {
+                ahead -= dma_count(T);  // in flight already: now the current task
+            } else {
+                // the slots of task t last held x of an earlier task: wait
+                // until every compute wave has entered the task after it
+                // (the gate); a task that reads earlier outputs waits until
+                // they have finished t - 1 (entered t, stores complete).
+                // Nothing is in flight here.
+                const bool wait = DEP && ctl_wait(T.ctl);
+                const int need = wait ? t : ctl_gate(T.ctl);
+                uint32_t spins = 0;
+                while (!all_entered(need)) {
+                    if (++spins == kSpinLimit) {
+                        fail();
+                        break;
                     }
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if (wait) {
+                    // grid barrier between the loaders: this workgroup's
+                    // outputs are released with the arrival, the others'
+                    // acquired after it
+                    ++nbar;
+                    if (lane == 0) {
+                        __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                        const uint32_t target = (uint32_t)nbar * gridDim.x;
+                        uint32_t gspins = 0;
+                        while (__hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                               target) {
+                            if (++gspins == kSpinLimit) {
+                                fail();
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(1);
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                }
+                chain_dma_x(T, xb, lane);
+                issued = t + 1;
             }
-            copy_x(t);
+            issue_ahead();
+            publish(t);
         }
     } else {
         // ---------------------------------------------------------- compute
@@ -1006,18 +1116,19 @@ void gemv_chain_kernel(const ChainArgs a)
         // differ from task to task.
         // tv: the views of the newest position's task (positions are made
         // and loaded in order, so the newest is always the one loaded)
-        TaskViews tv = task_views<FMT>(a.t[0], a.gshift);
+        TaskViews tv = task_views<FMT>(task(0), a.gshift);
         auto first_pos = [&](int t) {
             for (; t < nt; ++t) {
                 const int e =
                     (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
-                if (e < a.t[t].N) {
-                    tv = task_views<FMT>(a.t[t], a.gshift);
-                    return CPos{t, e, 0, tv.S == 1, tv.y + e};
+                const ChainTask T = task(t);
+                if (e < T.N) {
+                    tv = task_views<FMT>(T, a.gshift);
+                    return CPos{t, e, 0, tv.S == 1, tv.y + e, tv.xbase};
                 }
             }
             // past the last task: a row past the end of the last views
-            return CPos{nt, tv.N, 0, false, tv.y};
+            return CPos{nt, tv.N, 0, false, tv.y, 0};
         };
         auto advance = [&](CPos q) {
             if (q.t >= nt)
@@ -1056,12 +1167,12 @@ void gemv_chain_kernel(const ChainArgs a)
         // first (the loader releases them to the grid).
         auto enter = [&]() {
             const int t = ++cur;
-            if (DEP && a.t[t].wait)
+            if (DEP && ctl_wait(task(t).ctl))
                 wait_vm<0>();
             if (lane == 0)
-                __hip_atomic_fetch_add(&entered[t & 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&entered[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             uint32_t spins = 0;
-            while (__hip_atomic_load(&ready[t & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != t) {
+            while (__hip_atomic_load(&ready[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 1) {
                 if (++spins == kSpinLimit) {
                     fail();
                     break;
@@ -1097,7 +1208,7 @@ void gemv_chain_kernel(const ChainArgs a)
                 }
                 const int key = 8 * cp.t + cp.s;
                 if (key != xkey) {
-                    chain_x_slice(xreg, xinv_reg, xb[cp.t & 1], xinv_lds[cp.t & 1], cp.s, lane);
+                    chain_x_slice(xreg, xinv_reg, xb, xinv_lds, cp.xbase, cp.s, lane);
                     xkey = key;
                 }
                 const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
@@ -1109,7 +1220,10 @@ void gemv_chain_kernel(const ChainArgs a)
                     const float out = wave_sum(acc[0]);
                     acc[0] = 0.0f;
                     if (live && lane == 0)
-                        *cp.yp = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                        // through a global (not flat) pointer: a flat store may
+                        // write LDS, so LDS reads after it would wait for it
+                        *(__attribute__((address_space(1))) uint16_t *)cp.yp =
+                            (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
                 }
                 pos[q] = advance(pos[(q + P - 1) % P]);
                 load_pos(st[q], pos[q]);
@@ -1201,7 +1315,7 @@ hipError_t launch_chain_t(const ChainArgs &args, hipStream_t s)
         return hipErrorInvalidDevice;
     bool dep = false;
     for (int i = 1; i < args.ntasks; ++i)
-        dep = dep || args.t[i].wait;
+        dep = dep || (args.t[i].ctl & 1);
     void *kargs[] = {const_cast<ChainArgs *>(&args)};
     const void *fn = dep ? (const void *)gemv_chain_kernel<FMT, ACT, depth, true>
                          : (const void *)gemv_chain_kernel<FMT, ACT, depth, false>;
@@ -1217,14 +1331,28 @@ hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_t
 {
     ChainArgs a = {};
     a.gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
+    int base = 0, last_user[kChainSlots];
+    for (int sl = 0; sl < kChainSlots; ++sl)
+        last_user[sl] = -1;
     for (int i = 0; i < ntasks; ++i) {
         // double-quantized absmax: the constants' base in place of zeros
         const uint8_t *z = f == Q4_NF4_DQ ? (const uint8_t *)tasks[i].scales +
                                                 dq_s2_offset(tasks[i].N * (tasks[i].K >> a.gshift))
                                           : tasks[i].zeros;
+        // x slots: task i's stages take consecutive slots (mod 8) after task
+        // i - 1's; the gate is the task after the last one that used any of
+        // them (every task has at most 4 stages, so that is at most i - 1)
+        const int S = chain_stages((int)tasks[i].K);
+        int last = -1;
+        for (int st = 0; st < S; ++st) {
+            const int sl = (base + st) % kChainSlots;
+            last = last_user[sl] > last ? last_user[sl] : last;
+            last_user[sl] = i;
+        }
+        const int ctl = ((tasks[i].flags & Q4_TASK_NO_WAIT) ? 0 : 1) | (base << 1) | ((last + 1) << 8);
+        base = (base + S) % kChainSlots;
         a.t[i] = ChainTask{(const uint16_t *)tasks[i].x, tasks[i].codes, tasks[i].scales, z,
-                           (uint16_t *)tasks[i].y, (int)tasks[i].N, (int)tasks[i].K,
-                           (tasks[i].flags & Q4_TASK_NO_WAIT) ? 0 : 1};
+                           (uint16_t *)tasks[i].y, (int)tasks[i].N, (int)tasks[i].K, ctl};
     }
     a.ntasks = ntasks;
     a.sync = sync;

@@ -102,6 +102,44 @@ def test_chain_no_wait_flag():
     _assert_same(outs, ref, "no-wait")
 
 
+# (N, K) of a long run of independent tasks: x slots reused many times over,
+# runs of four-stage tasks (each slot set freed only by the task before),
+# one-stage tasks (several in flight at once), three-stage tasks that wrap
+# the slots, and tasks of a few rows that most waves only pass through
+SLOT_SHAPES = ([(700, 16384)] * 3 + [(1500, 4096)] * 10 + [(257, 11008), (1, 1024), (3000, 11008),
+               (900, 8192), (64, 16384), (2051, 2176), (5, 4096)] + [(333, 2176)] * 6)
+
+
+@pytest.mark.parametrize("fmt,g,act", [(q4.NF4, 64, q4.BF16), (q4.INT4_SYM, 128, q4.F16),
+                                       (q4.NF4_DQ, 32, q4.BF16)])
+def test_chain_slot_reuse(fmt, g, act):
+    """Independent tasks of mixed stage counts (their x prefetched into the
+    LDS slots while earlier tasks run), with a task reading an earlier
+    output in the middle, give the bits of consecutive GEMVs."""
+    tasks, ref = [], []
+    for i, (N, K) in enumerate(SLOT_SHAPES):
+        q = _weight(N, K, fmt, g, 7000 + 17 * i)
+        x = _x(K, act, 7100 + i)
+        y = torch.full((1, N), 7.0, dtype=TORCH_ACT[act], device=DEV)
+        tasks.append((x, q, y, q4.TASK_NO_WAIT))
+        ref.append(q4.gemv(x, q))
+    # after the tenth task: one reading the first one-stage task's output
+    # (N = 1500 -> K = 1500 is not a whole number of groups; 1024 of it is)
+    src = tasks[3][2][:, :1024]
+    qd = _weight(400, 1024, fmt, g, 7999)
+    yd = torch.empty((1, 400), dtype=TORCH_ACT[act], device=DEV)
+    tasks.insert(10, (src, qd, yd, 0))
+    ref.insert(10, q4.gemv(ref[3][:, :1024].contiguous(), qd))
+    sync = q4.chain_sync(DEV)
+    for rep in range(2):
+        for t in tasks:
+            t[2].fill_(7.0)
+        outs = q4.gemv_chain(tasks, sync=sync)
+        torch.cuda.synchronize()
+        _assert_same(outs, ref, f"slots fmt{fmt} g{g} rep{rep}")
+        assert sync.cpu().tolist() == [0, 0, 0, 0]
+
+
 def test_chain_longest():
     """Q4_GEMV_CHAIN_MAX tasks, each reading the previous task's y."""
     fmt, g, act = q4.INT4_ASYM, 32, q4.F16
