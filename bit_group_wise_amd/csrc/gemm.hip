@@ -73,8 +73,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// Position of 16-byte chunk c of staged x row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Position of 16-byte chunk c of staged x row r (and the chunk at position c):
+// c XOR a 3-bit key from bits 1-3 of r.  A fragment read (lane l: row l & 15,
+// chunk 2 (l >> 4) + h) then puts the rows that share a 128-bank line
+// (r, r + 4, r + 8, r + 12) on distinct 16-byte positions for each pair of
+// lane quads, and the 8 rows of one parity on 8 distinct positions: no bank
+// conflicts.  (A key of (r >> 1) & 7 cost about 4 conflict cycles per read.)
+__device__ __forceinline__ int swz_key(int r) { return ((r >> 2) & 1) | (r & 2) | (((r >> 3) & 1) << 2); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ swz_key(r); }
 
 // Scale / zero-point layout of one 256-k span of a row.
 template <int FMT, int G>
@@ -390,13 +396,13 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
         }
     }
     // x DMA: lane l of 1 KB block B is row 8 B + l / 8, position l % 8,
-    // holding chunk (l % 8) ^ (((8 B + l / 8) >> 1) & 7); the row's swizzle
-    // key is 4 (B & 1) + l / 16
+    // holding chunk swz(8 B + l / 8, l % 8); bits 0-3 of the row are
+    // 8 (B & 1) + l / 8
     {
         const int rl = lane >> 3, p = lane & 7;
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            c.xv[e] = rl * 2 * K + 16 * (p ^ ((4 * e) | (lane >> 4)));
+            c.xv[e] = rl * 2 * K + 16 * swz(8 * e + rl, p);
     }
     // fragment reads: x row 16 i + fr, chunk 2 fq + h (the swizzle does not
     // depend on i)

@@ -217,6 +217,15 @@ __device__ __forceinline__ float keep_f32(float v)
 // Byte I of a dword as a float (v_cvt_f32_ubyte{0..3}).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) { return (float)((v >> (8 * I)) & 0xffu); }
+// The word itself, opaque to the optimizer (an empty register-only asm).
+// Keeps a word of byte-spread nibbles (w & 0x0f0f0f0f) whole: each byte then
+// converts with one v_cvt_f32_ubyteN, where the optimizer would otherwise
+// fold the mask into a 4-bit field extract (v_bfe) before every convert.
+__device__ __forceinline__ uint32_t opaque_word(uint32_t v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
 // Two fp32 -> packed pair (a in the low half).
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) { return f2h_bits(a) | (f2h_bits(b) << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b)

@@ -46,8 +46,8 @@ __device__ __forceinline__ void dequant8_f32(uint32_t w, float s, float bias, co
             v[2 * i + 1] = keep_f32(lp[i].y * s);
         }
     } else {
-        const uint32_t lo = w & 0x0f0f0f0fu;
-        const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;
+        const uint32_t lo = opaque_word(w & 0x0f0f0f0fu);
+        const uint32_t hi = opaque_word((w >> 4) & 0x0f0f0f0fu);
         v[0] = __builtin_fmaf(ubyte_f32<0>(lo), s, bias);
         v[1] = __builtin_fmaf(ubyte_f32<0>(hi), s, bias);
         v[2] = __builtin_fmaf(ubyte_f32<1>(lo), s, bias);
