@@ -226,6 +226,14 @@ __device__ __forceinline__ uint32_t opaque_word(uint32_t v)
     asm("" : "+v"(v));
     return v;
 }
+// A wave-uniform constant kept in a scalar register (so that an instruction
+// that also takes a constant in a vector register can read it).
+__device__ __forceinline__ uint32_t opaque_sword(uint32_t v)
+{
+    asm("" : "+s"(v));
+    return v;
+}
+
 // Two fp32 -> packed pair (a in the low half).
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) { return f2h_bits(a) | (f2h_bits(b) << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b)

@@ -46,16 +46,33 @@ __device__ __forceinline__ void dequant8_f32(uint32_t w, float s, float bias, co
             v[2 * i + 1] = keep_f32(lp[i].y * s);
         }
     } else {
-        const uint32_t lo = opaque_word(w & 0x0f0f0f0fu);
-        const uint32_t hi = opaque_word((w >> 4) & 0x0f0f0f0fu);
-        v[0] = __builtin_fmaf(ubyte_f32<0>(lo), s, bias);
-        v[1] = __builtin_fmaf(ubyte_f32<0>(hi), s, bias);
-        v[2] = __builtin_fmaf(ubyte_f32<1>(lo), s, bias);
-        v[3] = __builtin_fmaf(ubyte_f32<1>(hi), s, bias);
-        v[4] = __builtin_fmaf(ubyte_f32<2>(lo), s, bias);
-        v[5] = __builtin_fmaf(ubyte_f32<2>(hi), s, bias);
-        v[6] = __builtin_fmaf(ubyte_f32<3>(lo), s, bias);
-        v[7] = __builtin_fmaf(ubyte_f32<3>(hi), s, bias);
+        // (q - z) s as one exact fma per weight on an fp16 operand.  OR-ing
+        // a nibble into 0x6400 makes the fp16 1024 + q (low nibble of a
+        // byte) or 1024 + 16 q (high nibble), and
+        //   fma(1024 + q, s, -(1024 + z) s),  fma(1024 + 16 q, s / 16, -(64 + z) s)
+        // have exact terms ((q - z) s needs at most 15 significant bits, the
+        // biases at most 22), so each returns the binary32 product itself.
+        // v_fma_mix_f32 reads the fp16 from either half of a word: 5
+        // instructions unpack 8 weights (with the masks in registers, so
+        // that mask and OR fuse into one v_and_or_b32).
+        const uint32_t m1 = opaque_word(0x000f000fu), m2 = opaque_word(0x00f000f0u);
+        const uint32_t one = opaque_sword(0x64006400u);
+        const uint32_t w8 = w >> 8;
+        const f16x2 d0 = std::bit_cast<f16x2>((w & m1) | one);   // q0, q4
+        const f16x2 d1 = std::bit_cast<f16x2>((w & m2) | one);   // 16 q1, 16 q5
+        const f16x2 d2 = std::bit_cast<f16x2>((w8 & m1) | one);  // q2, q6
+        const f16x2 d3 = std::bit_cast<f16x2>((w8 & m2) | one);  // 16 q3, 16 q7
+        const float b1 = __builtin_fmaf(-1024.0f, s, bias);
+        const float s16 = s * 0.0625f;
+        const float b16 = __builtin_fmaf(-64.0f, s, bias);
+        v[0] = __builtin_fmaf((float)d0[0], s, b1);
+        v[1] = __builtin_fmaf((float)d1[0], s16, b16);
+        v[2] = __builtin_fmaf((float)d2[0], s, b1);
+        v[3] = __builtin_fmaf((float)d3[0], s16, b16);
+        v[4] = __builtin_fmaf((float)d0[1], s, b1);
+        v[5] = __builtin_fmaf((float)d1[1], s16, b16);
+        v[6] = __builtin_fmaf((float)d2[1], s, b1);
+        v[7] = __builtin_fmaf((float)d3[1], s16, b16);
     }
 }
 
