@@ -68,8 +68,8 @@ __device__ __forceinline__ int yswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// One thread's loads of a step: 4 x 16 bytes of dY (row t / 2, chunks
-// 4 (t & 1) .. + 3), and for weight rows 2p, 2p + 1 of the step (p = t % 32)
+// One thread's loads of a step: 4 x 16 bytes of dY (chunk t % 8 of rows
+// t / 8 + 64 i), and for weight rows 2p, 2p + 1 of the step (p = t % 32)
 // the code dword of columns 8 cq .. 8 cq + 7 (cq = t / 32) with its group's
 // scale (NF4: fp32 bits, INT4: fp16 bits, NF4_DQ: the 8-bit code) and
 // zero-point byte (asym) or run constant (NF4_DQ).
@@ -93,14 +93,14 @@ __device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0_, in
     // in a loop over the lanes' values of their scalar offset)
     const int n0 = __builtin_amdgcn_readfirstlane(n0_);
     const int t = threadIdx.x;
-    // dY: elements n0 + 8 chunk .. of row t / 2 of the tile (rows past M and
-    // elements past the buffer read zeros; elements past N of a row read the
-    // next row, which meets zero weights)
-    const int yrow = t >> 1;
+    // dY: elements n0 + 8 (t % 8) .. + 7 of rows t / 8 + 64 i of the tile,
+    // 8 lanes to a row, so that each 16-byte LDS store instruction fills 8
+    // whole rows (rows past M and elements past the buffer read zeros;
+    // elements past N of a row read the next row, which meets zero weights)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int ch = 4 * (t & 1) + i;
-        ld.y[i] = __builtin_amdgcn_raw_buffer_load_b128(c.yr, 2 * (yrow * c.N + 8 * ch), 2 * n0, 0);
+        const int yrow = (t >> 3) + 64 * i;
+        ld.y[i] = __builtin_amdgcn_raw_buffer_load_b128(c.yr, 2 * (yrow * c.N + 8 * (t & 7)), 2 * n0, 0);
     }
     // weights: row n0 + t / 8 of the step, columns k0 + 16 (t % 8) .. + 15
     // (8 lanes read a row's 64 bytes of the tile together).  Rows past N
@@ -226,7 +226,6 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
             for (int f = 0; f < kWMF; ++f)
                 acc[j][f] = mfma<ACT>(fa[j], fb[f], acc[j][f]);
         };
-        const int yr = t >> 1;
         // the weight row piece of the next step: 16 columns of row t / 8,
         // dequantized (pairs along k, as q4_dequantize writes them) and
         // written as two 16-byte pieces
@@ -259,7 +258,8 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
         for (int j = 0; j < kKF; ++j) {
             mfmas(j);
             // dY of the next step, one 16-byte piece per group of MFMAs
-            *(u32x4 *)(ysn + yr * kYRow + 16 * yswz(yr, 4 * (t & 1) + j)) = ld.y[j];
+            const int yr = (t >> 3) + 64 * j;
+            *(u32x4 *)(ysn + yr * kYRow + 16 * yswz(yr, t & 7)) = ld.y[j];
             __builtin_amdgcn_sched_barrier(0);
         }
         reads(1);
@@ -292,10 +292,11 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
     __syncthreads();  // the level-pair table
     {
         // step 0 into buffer 0 (no products yet)
-        const int yr = t >> 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(u32x4 *)(ys[0] + yr * kYRow + 16 * yswz(yr, 4 * (t & 1) + i)) = la.y[i];
+        for (int i = 0; i < 4; ++i) {
+            const int yr = (t >> 3) + 64 * i;
+            *(u32x4 *)(ys[0] + yr * kYRow + 16 * yswz(yr, t & 7)) = la.y[i];
+        }
         float sc, bias = 0.0f;
         if constexpr (FMT == Q4_NF4) {
             sc = std::bit_cast<float>(la.s);
