@@ -1023,6 +1023,51 @@ void gemv_chain_kernel(const ChainArgs a)
     __syncthreads();
     auto task = [&](int t) { return lds_task(lds.tasks, t); };
 
+    // The rows this workgroup works on.  With no task waiting for earlier
+    // outputs, each workgroup takes one contiguous block of the tasks' rows
+    // laid end to end, [(tlo, rlo), (tend, rend)), balanced by stage count:
+    // a wave then meets a new task once or twice per launch rather than at
+    // almost every row of a short task (each switch reads the task's
+    // descriptor and x slice and waits for its x, inside the ring).  A chain
+    // with waits keeps the walk of every task over all waves, since the
+    // whole grid finishes a task before a waiting one starts.
+    int tlo = 0, rlo = 0, tend = nt, rend = 0;
+    if constexpr (!DEP) {
+        // first row whose start (in stages, rows laid end to end) is at or
+        // after `target`
+        auto locate = [&](int64_t target, int &u, int &r) {
+            int64_t acc = 0;
+            for (u = 0; u < nt; ++u) {
+                const ChainTask U = task(u);
+                const int S = chain_stages(U.K);
+                const int64_t span = (int64_t)U.N * S;
+                if (target < acc + span) {
+                    const int64_t rr = (target - acc + S - 1) / S;
+                    if (rr < U.N) {
+                        r = (int)rr;
+                    } else {
+                        r = 0;
+                        ++u;
+                    }
+                    return;
+                }
+                acc += span;
+            }
+            u = nt;
+            r = 0;
+        };
+        int64_t total = 0;
+        for (int u = 0; u < nt; ++u) {
+            const ChainTask U = task(u);
+            total += (int64_t)U.N * chain_stages(U.K);
+        }
+        locate(total * blockIdx.x / gridDim.x, tlo, rlo);
+        locate(total * (blockIdx.x + 1) / gridDim.x, tend, rend);
+    }
+    const bool has_rows = tlo < tend || (tlo == tend && rlo < rend);
+    // the tasks this workgroup loads and enters: tlo .. thi
+    const int thi = !has_rows ? tlo - 1 : (rend == 0 ? tend - 1 : tend);
+
     if (wave == kChainCompute) {
         // ---------------------------------------------------------- loader
         // x goes in by DMA as early as the slots allow: a later task's as
@@ -1033,7 +1078,7 @@ void gemv_chain_kernel(const ChainArgs a)
         int ahead = 0;   // DMA instructions in flight for tasks after the current one
         auto dma_count = [&](const ChainTask &T) { return kChainDmaPerStage * chain_stages(T.K); };
         auto issue_ahead = [&]() {
-            while (issued < nt) {
+            while (issued <= thi) {
                 const ChainTask T = task(issued);
                 const int n = dma_count(T);
                 if ((DEP && ctl_wait(T.ctl)) || ahead + n > kChainDmaAhead || !all_entered(ctl_gate(T.ctl)))
@@ -1050,16 +1095,21 @@ void gemv_chain_kernel(const ChainArgs a)
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __hip_atomic_store(&ready[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
-        // task 0 is entered by every compute wave in the prologue
-        entered[lane] = lane == 0 ? kChainCompute : 0;
+        // task tlo is entered by every compute wave in the prologue; the
+        // tasks before it are never entered here (they count as entered,
+        // for the gates of the slots they would have used)
+        entered[lane] = lane <= tlo ? kChainCompute : 0;
         ready[lane] = 0;
-        chain_dma_x(task(0), xb, lane);
-        issued = 1;
-        issue_ahead();
-        publish(0);
-        __syncthreads();  // the table, the counters and x of task 0
+        issued = tlo;
+        if (has_rows) {
+            chain_dma_x(task(tlo), xb, lane);
+            issued = tlo + 1;
+            issue_ahead();
+            publish(tlo);
+        }
+        __syncthreads();  // the table, the counters and x of task tlo
         int nbar = 0;
-        for (int t = 1; t < nt; ++t) {
+        for (int t = tlo + 1; t <= thi; ++t) {
             const ChainTask T = task(t);
             if (issued > t) {
                 ahead -= dma_count(T);  // in flight already: now the current task
@@ -1110,14 +1160,37 @@ void gemv_chain_kernel(const ChainArgs a)
         // vector-memory instructions per ring refill
         const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * kChainCompute + wave);
         const int total_waves = gridDim.x * kChainCompute;
-        // A wave's walk: task by task, its rows of the task and each row's
-        // stages.  Task t's rows are dealt to the waves from a rotated
-        // start, so that the waves holding one row more than the others
-        // differ from task to task.
+        // A wave's walk: its rows in order and each row's stages.  With no
+        // waiting task, the rows are those of the workgroup's block, dealt
+        // to its waves in turn.  Otherwise the walk goes task by task: task
+        // t's rows are dealt to all the grid's waves from a rotated start,
+        // so that the waves holding one row more than the others differ
+        // from task to task.
         // tv: the views of the newest position's task (positions are made
         // and loaded in order, so the newest is always the one loaded)
-        TaskViews tv = task_views<FMT>(task(0), a.gshift);
+        TaskViews tv = task_views<FMT>(task(tlo < nt ? tlo : 0), a.gshift);
+        // a position past this wave's rows: a row past the end of the
+        // current views
+        auto past = [&]() { return CPos{nt, tv.N, 0, false, tv.y, 0}; };
+        // blocked walk: wave w takes rows w, w + 15, ... of the block
+        auto in_block = [&](int u, int r) { return u < tend || (u == tend && r < rend); };
+        auto block_pos = [&](int u, int r) {
+            // row r of task u, or the first row after it when r >= N_u
+            while (u < nt) {
+                const int n = task(u).N;
+                if (r < n)
+                    break;
+                r -= n;
+                ++u;
+            }
+            if (!in_block(u, r))
+                return past();
+            tv = task_views<FMT>(task(u), a.gshift);
+            return CPos{u, r, 0, tv.S == 1, tv.y + r, tv.xbase};
+        };
         auto first_pos = [&](int t) {
+            if constexpr (!DEP)
+                return has_rows ? block_pos(tlo, rlo + wave) : past();
             for (; t < nt; ++t) {
                 const int e =
                     (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
@@ -1128,17 +1201,25 @@ void gemv_chain_kernel(const ChainArgs a)
                 }
             }
             // past the last task: a row past the end of the last views
-            return CPos{nt, tv.N, 0, false, tv.y, 0};
+            return past();
         };
         auto advance = [&](CPos q) {
             if (q.t >= nt)
                 return q;
             if (++q.s == tv.S) {
                 q.s = 0;
-                q.row += total_waves;
-                q.yp += total_waves;
-                if (q.row >= tv.N)
-                    return first_pos(q.t + 1);
+                if constexpr (!DEP) {
+                    const int r = q.row + kChainCompute;
+                    if (r >= tv.N || !in_block(q.t, r))
+                        return block_pos(q.t, r);
+                    q.row = r;
+                    q.yp += kChainCompute;
+                } else {
+                    q.row += total_waves;
+                    q.yp += total_waves;
+                    if (q.row >= tv.N)
+                        return first_pos(q.t + 1);
+                }
             }
             q.last = q.s == tv.S - 1;
             return q;
@@ -1160,8 +1241,8 @@ void gemv_chain_kernel(const ChainArgs a)
             st[q] = Stage{};
             load_pos(st[q], pos[q]);
         }
-        __syncthreads();  // the table, the counters and x of task 0
-        int cur = 0;
+        __syncthreads();  // the table, the counters and x of task tlo
+        int cur = tlo;
         // Entering task cur + 1: count in, then wait for its x.  Before a
         // task that reads earlier outputs, this wave's own stores complete
         // first (the loader releases them to the grid).
@@ -1230,7 +1311,7 @@ void gemv_chain_kernel(const ChainArgs a)
             }
         }
         // waves with no rows in the last tasks still count into them
-        while (cur < nt - 1)
+        while (cur < thi)
             enter();
     }
     wait_vm<0>();  // no LDS DMA may be in flight when the workgroup ends

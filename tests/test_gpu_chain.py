@@ -140,6 +140,33 @@ def test_chain_slot_reuse(fmt, g, act):
         assert sync.cpu().tolist() == [0, 0, 0, 0]
 
 
+@pytest.mark.parametrize("fmt,g,act", [(q4.NF4, 64, q4.BF16), (q4.INT4_ASYM, 32, q4.F16),
+                                       (q4.NF4_DQ, 64, q4.BF16)])
+def test_chain_blocked_rows(fmt, g, act):
+    """A chain with no waiting task deals each workgroup a contiguous block
+    of the tasks' rows (balanced by stage count): the blocks cross task
+    boundaries, rows of one to four stages mix, and in the small chains most
+    workgroups get no rows at all.  Outputs equal consecutive GEMVs."""
+    chains = [SLOT_SHAPES, [(1, 1024), (3, 16384), (5, 2176), (2, 11008), (1, 64 if g <= 64 else 128)],
+              [(7, 4096)], [(40000, 4096)]]
+    sync = q4.chain_sync(DEV)
+    for ci, shapes in enumerate(chains):
+        tasks, ref = [], []
+        for i, (N, K) in enumerate(shapes):
+            q = _weight(N, K, fmt, g, 8000 + 31 * ci + i)
+            x = _x(K, act, 8100 + 31 * ci + i)
+            y = torch.full((1, N), 7.0, dtype=TORCH_ACT[act], device=DEV)
+            tasks.append((x, q, y, q4.TASK_NO_WAIT))
+            ref.append(q4.gemv(x, q))
+        for rep in range(2):
+            for t in tasks:
+                t[2].fill_(7.0)
+            outs = q4.gemv_chain(tasks, sync=sync)
+            torch.cuda.synchronize()
+            _assert_same(outs, ref, f"blocked chain {ci} fmt{fmt} g{g} rep{rep}")
+            assert sync.cpu().tolist() == [0, 0, 0, 0]
+
+
 def test_chain_longest():
     """Q4_GEMV_CHAIN_MAX tasks, each reading the previous task's y."""
     fmt, g, act = q4.INT4_ASYM, 32, q4.F16
