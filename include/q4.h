@@ -185,8 +185,9 @@ q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t
  * the same stream; chains that may overlap (other streams) need their own.
  * Word 2 becomes nonzero if a wait between tasks gave up after about a second
  * (the grid could not make progress; y is then undefined) and stays set until
- * the caller clears it.  The chain is one cooperative launch of one
- * workgroup per compute unit: a launch the runtime refuses returns Q4_EHIP. */
+ * the caller clears it.  The chain is one launch of one workgroup per
+ * compute unit, cooperative when a task waits (its grid barrier needs every
+ * workgroup resident): a launch the runtime refuses returns Q4_EHIP. */
 #define Q4_GEMV_CHAIN_MAX 64
 #define Q4_GEMV_CHAIN_MAX_K 16384
 #define Q4_GEMV_CHAIN_MAX_CODES 2147483519LL /* 2^31 - 129 */
