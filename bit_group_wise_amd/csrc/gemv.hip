@@ -669,16 +669,17 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 // x sits in LDS in 8 slots of one stage each (8 KB); task t's stages take
 // consecutive slots from slot base_t on (mod 8), tasks in turn, so a slot is
 // reused only by a task at least two later.  The loader copies x of task t
-// once every compute wave has entered the task after the last one that used
-// those slots (the gate, computed on the host) and publishes it; a compute
-// wave entering task t waits only for that.  So waves may drift several
-// tasks apart: with a double buffer they could not get more than one task
-// ahead of the slowest, and a task of about one row per wave ran at the
-// pace of the waves that got two.  For a task that reads earlier outputs
-// the loader first waits until every compute wave has finished the earlier
-// tasks, then for the whole grid (a grid barrier between loader waves).
-// The compute waves never wait for each other.  The table is filled once
-// per launch.
+// (by DMA, as early as the slots allow) once every compute wave has entered
+// the task after the last one that used those slots (the gate, computed on
+// the host) and publishes it; a compute wave entering task t waits only for
+// that.  So waves may drift several tasks apart.  With no task waiting for
+// earlier outputs, each workgroup works on one contiguous block of the
+// tasks' rows and loads and enters only the block's tasks.  Otherwise every
+// task's rows are spread over all waves, and for a task that reads earlier
+// outputs the loader first waits until every compute wave has finished the
+// earlier tasks, then for the whole grid (a grid barrier between loader
+// waves).  The compute waves never wait for each other.  The table is
+// filled once per launch.
 struct ChainTask {
     const uint16_t *x;
     const uint8_t *codes;
