@@ -214,18 +214,20 @@ def main():
     if sync.cpu().tolist() != [0, 0, 0, 0]:
         raise RuntimeError(f"chain sync words not clear: {sync.cpu().tolist()}")
 
-    # each chained launch of the timed steps is bracketed by its own events
-    # on the launch stream (the kernel's average launch duration)
-    lev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in indep] for _ in range(args.steps)]
+    # the chained launches of the timed steps are separated by events on the
+    # launch stream, one before the first and one after each (the kernel's
+    # average launch duration; a launch's span then also holds the short
+    # dispatch gap after the previous one)
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(indep) + 1)]
+           for _ in range(args.steps)]
 
     def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
         for i, c in enumerate(indep):
-            if evs is not None:
-                evs[i][0].record(stream)
             q4.gemv_chain(c, sync=sync)
             if evs is not None:
-                evs[i][1].record(stream)
+                evs[i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -269,7 +271,7 @@ def main():
         raise RuntimeError("double-quantized chain differs from single-product launches")
     del ref_dq
     dq_ms = timed(lambda: run_chains(chains_dq), max(args.steps // 2, 3))
-    launch_ms = [a.elapsed_time(b) for evs in lev for a, b in evs]
+    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for evs in lev for i in range(len(indep))]
     chain_avg_us = sum(launch_ms) / len(launch_ms) * 1e3
     bytes_per_chain = w_bytes / n_chain
     chain_gbs = bytes_per_chain / (chain_avg_us * 1e-6) / 1e9
