@@ -349,8 +349,9 @@ def main():
 def _timer(torch, stream):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def timed(fn, reps):
-        fn()
+    def timed(fn, reps, warm=1):
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(reps):
@@ -495,7 +496,9 @@ def extra_legs(torch, q4, dev, stream):
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     dt = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 10)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    gt = timed(lambda: q4.gemm(x, q, out=y), 10)
+    # matrix-core legs: steady state after 20 warm-up calls (the first
+    # calls after idle run at a lower clock)
+    gt = timed(lambda: q4.gemm(x, q, out=y), 30, warm=20)
     flops = 2.0 * M * N * K
     codec_bytes = N * K * 2 + q.nbytes()
     # the pages' unfused path: dequantize to the compute dtype, then a
@@ -505,8 +508,8 @@ def extra_legs(torch, q4, dev, stream):
     def unfused():
         q4.dequantize(q, torch.bfloat16, out=out)
         torch.matmul(x, out.t(), out=yb)
-    ut = timed(unfused, 10)
-    mt = timed(lambda: torch.matmul(x, out.t(), out=yb), 10)
+    ut = timed(unfused, 30, warm=20)
+    mt = timed(lambda: torch.matmul(x, out.t(), out=yb), 30, warm=20)
     # the same at decode width: M = 16 on the c3 gate/up shape (NF4 g64)
     w16 = torch.empty((11008, 4096), dtype=torch.float16, device=dev).normal_(0.0, 0.02)
     q16 = q4.quantize(w16, q4.NF4, 64)
@@ -526,12 +529,12 @@ def extra_legs(torch, q4, dev, stream):
     dy = torch.empty((M, N), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
     dy = dy.to(torch.bfloat16)
     dxo = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    bt = timed(lambda: q4.gemm_dx(dy, q, out=dxo), 10)
+    bt = timed(lambda: q4.gemm_dx(dy, q, out=dxo), 30, warm=20)
 
     def unfused_dx():
         q4.dequantize(q, torch.bfloat16, out=out)
         torch.matmul(dy, out, out=dxo)
-    but = timed(unfused_dx, 10)
+    but = timed(unfused_dx, 30, warm=20)
     return {
         "gemm_dx": {"shape": f"dY {M}x{N} . W {N}x{K} int4_asym g32 bf16", "ms": round(bt, 4),
                     "TFLOPs": round(flops / (bt * 1e-3) / 1e12, 1),
