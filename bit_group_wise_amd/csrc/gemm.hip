@@ -63,13 +63,26 @@ constexpr int kWRows = 16 * kNF;              // W rows per wave (32)
 constexpr int kSpan = 4;                      // steps per scale / zero-point span
 constexpr int kSpanK = kSpan * BK;            // 256
 
-// Buffer resource over [base, base + bytes).  The range check is per dword:
-// a dword not wholly inside the view reads as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+// A buffer view: base and length in bytes (at most 2^32 - 1; the host
+// bounds K so that every view of a tile fits).  Loads go through a resource
+// over [base + off, base + bytes) for the load's wave-uniform offset `off`:
+// the buffer unit range-checks only the lane's offset (voffset), not a
+// load's soffset, so a uniform part that may pass the end of the view
+// moves the view instead.  The range check is per dword: a dword not
+// wholly inside the view reads as zero.
+struct View {
+    const char *base;
+    uint32_t bytes;
+};
+__device__ __forceinline__ View make_view(const void *base, int64_t bytes)
 {
-    const int64_t cap = 0x7fffffffll;
-    const uint32_t n = bytes <= 0 ? 0u : (uint32_t)(bytes > cap ? cap : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+    const int64_t cap = 0xffffffffll;
+    return View{(const char *)base, (uint32_t)(bytes <= 0 ? 0 : (bytes > cap ? cap : bytes))};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t at(const View &v, uint32_t off)
+{
+    const uint32_t n = off < v.bytes ? v.bytes - off : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(v.base + off), (short)0, (int)n,
                                              0x00020000);
 }
 
@@ -113,10 +126,10 @@ struct MSpan {
 };
 
 // Per-thread constants of the tile.  Every load address is a lane constant
-// (voffset) plus a wave-uniform part (soffset), so the loads cost no vector
-// arithmetic.
+// (voffset) plus a wave-uniform part that moves the view (scalar
+// arithmetic), so the loads cost no vector arithmetic.
 struct TileCtx {
-    __amdgpu_buffer_rsrc_t xr, cr, sr, zr;
+    View xr, cr, sr, zr;
     int K, Gn;   // K and groups per row
     int xv[2];   // x DMA: voffset for even / odd blocks
     int rd[2];   // fragment reads: LDS byte offset of half step h (+2048 per fragment)
@@ -136,15 +149,16 @@ __device__ __forceinline__ void load_x1(const TileCtx &c, char *xn, int wave, in
 {
     const int B = kXBlocks * wave + i;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        c.xr, (__attribute__((address_space(3))) void *)(xn + 1024 * B), 16, c.xv[i & 1],
-        B * 16 * c.K + 2 * k0, 0, 0);
+        at(c.xr, (uint32_t)(B * 16 * c.K + 2 * k0)),
+        (__attribute__((address_space(3))) void *)(xn + 1024 * B), 16, c.xv[i & 1], 0, 0, 0);
 }
 
 // Codes of fragment j at step k0 (fragment j's rows are 4 j below
 // fragment 0's).
 __device__ __forceinline__ void load_codes(WStep &ws, int j, const TileCtx &c, int k0)
 {
-    ws.cw[j] = __builtin_amdgcn_raw_buffer_load_b64(c.cr, c.cv, 4 * j * (c.K >> 1) + (k0 >> 1), 0);
+    ws.cw[j] = __builtin_amdgcn_raw_buffer_load_b64(at(c.cr, (uint32_t)(4 * j * (c.K >> 1) + (k0 >> 1))),
+                                                    c.cv, 0, 0);
 }
 
 // Scales and zero-points of fragment j for the span starting at k0.
@@ -157,31 +171,31 @@ __device__ __forceinline__ void load_span(MSpan<FMT, G> &ms, int j, const TileCt
     if constexpr (S::sdw >= 4) {
 #pragma unroll
         for (int q = 0; q < S::sdw / 4; ++q) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(c.sr, c.sv, so + 16 * q, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(at(c.sr, (uint32_t)(so + 16 * q)), c.sv, 0, 0);
             ms.s[j][4 * q] = v[0];
             ms.s[j][4 * q + 1] = v[1];
             ms.s[j][4 * q + 2] = v[2];
             ms.s[j][4 * q + 3] = v[3];
         }
     } else if constexpr (S::sdw == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(c.sr, c.sv, so, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(at(c.sr, (uint32_t)so), c.sv, 0, 0);
         ms.s[j][0] = v[0];
         ms.s[j][1] = v[1];
     } else {
-        ms.s[j][0] = __builtin_amdgcn_raw_buffer_load_b32(c.sr, c.sv, so, 0);
+        ms.s[j][0] = __builtin_amdgcn_raw_buffer_load_b32(at(c.sr, (uint32_t)so), c.sv, 0, 0);
     }
     if constexpr (FMT == Q4_INT4_ASYM) {
         // ng nibbles from nibble zo of the first byte: 9 nibbles (5 bytes) at
         // most
         if constexpr (S::ng == 8)
-            ms.z[j] = __builtin_amdgcn_raw_buffer_load_b64(c.zr, c.zv, ug >> 1, 0);
+            ms.z[j] = __builtin_amdgcn_raw_buffer_load_b64(at(c.zr, (uint32_t)(ug >> 1)), c.zv, 0, 0);
         else
-            ms.z[j] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(c.zr, c.zv, ug >> 1, 0), 0u};
+            ms.z[j] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(at(c.zr, (uint32_t)(ug >> 1)), c.zv, 0, 0), 0u};
     }
     if constexpr (FMT == Q4_NF4_DQ) {
         // the span's groups (at most 8) lie in one run or straddle into the
         // next: both constants, from the run of the first group
-        ms.z[j] = __builtin_amdgcn_raw_buffer_load_b64(c.zr, 4 * ((c.zv + ug) / kDqRun), 0, 0);
+        ms.z[j] = __builtin_amdgcn_raw_buffer_load_b64(at(c.zr, 0), 4 * ((c.zv + ug) / kDqRun), 0, 0);
     }
 }
 
@@ -357,22 +371,22 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
     // the end (such a dword would read as zero).
     const int64_t mrows = M - m0 < BM ? M - m0 : BM;
     const int64_t nrows = N - n0 < BN ? N - n0 : BN;
-    c.xr = make_rsrc(x + (int64_t)m0 * K, mrows * K * 2);
-    c.cr = make_rsrc(codes + (int64_t)n0 * (K >> 1), nrows * (K >> 1));
+    c.xr = make_view(x + (int64_t)m0 * K, mrows * K * 2);
+    c.cr = make_view(codes + (int64_t)n0 * (K >> 1), nrows * (K >> 1));
     const int64_t s_total = FMT == Q4_NF4_DQ ? padded_meta_bytes(dq_scales_bytes((int64_t)N * Gn))
                                              : padded_meta_bytes((int64_t)N * Gn * S::ss);
-    c.sr = make_rsrc((const char *)scales + (int64_t)n0 * Gn * S::ss,
+    c.sr = make_view((const char *)scales + (int64_t)n0 * Gn * S::ss,
                      s_total - (int64_t)n0 * Gn * S::ss);
     const int64_t zg0 = (int64_t)n0 * Gn;  // flat group index of the tile's first group
     if constexpr (FMT == Q4_INT4_ASYM) {
         const int64_t z_total = padded_meta_bytes(((int64_t)N * Gn + 1) / 2);
-        c.zr = make_rsrc(zeros + (zg0 >> 1), z_total - (zg0 >> 1));
+        c.zr = make_view(zeros + (zg0 >> 1), z_total - (zg0 >> 1));
     } else if constexpr (FMT == Q4_NF4_DQ) {
         // second-level constants from the run of the tile's first group to
         // the end of the padded buffer (the 8-byte load of the last run
         // reads into the padding)
         const int64_t o2 = dq_s2_offset((int64_t)N * Gn) + 4 * (zg0 / kDqRun);
-        c.zr = make_rsrc((const char *)scales + o2, s_total - o2);
+        c.zr = make_view((const char *)scales + o2, s_total - o2);
     } else {
         c.zr = c.sr;
     }

@@ -81,7 +81,12 @@ struct DxLoads {
 };
 
 struct DxCtx {
-    __amdgpu_buffer_rsrc_t yr, cr, sr, zr;
+    // dY: the tile's rows, as base and length (a step's column offset moves
+    // the view: the buffer unit range-checks the lane's offset only, not a
+    // load's soffset)
+    const char *yb;
+    uint32_t ybytes;
+    __amdgpu_buffer_rsrc_t cr, sr, zr;
     int N, K, G, gshift;
     int p, cq;
 };
@@ -97,10 +102,12 @@ __device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0_, in
     // 8 lanes to a row, so that each 16-byte LDS store instruction fills 8
     // whole rows (rows past M and elements past the buffer read zeros;
     // elements past N of a row read the next row, which meets zero weights)
+    const uint32_t yoff = 2u * (uint32_t)n0;
+    const __amdgpu_buffer_rsrc_t yr = dx_rsrc(c.yb + yoff, yoff < c.ybytes ? c.ybytes - yoff : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int yrow = (t >> 3) + 64 * i;
-        ld.y[i] = __builtin_amdgcn_raw_buffer_load_b128(c.yr, 2 * (yrow * c.N + 8 * (t & 7)), 2 * n0, 0);
+        ld.y[i] = __builtin_amdgcn_raw_buffer_load_b128(yr, 2 * (yrow * c.N + 8 * (t & 7)), 0, 0);
     }
     // weights: row n0 + t / 8 of the step, columns k0 + 16 (t % 8) .. + 15
     // (8 lanes read a row's 64 bytes of the tile together).  Rows past N
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
     c.cq = t >> 5;
     const int64_t ngroups = (int64_t)N * c.G;
     const int mrows = M - m0 < TM ? M - m0 : TM;
-    c.yr = dx_rsrc(dy + (int64_t)m0 * N, (int64_t)mrows * N * 2);
+    c.yb = (const char *)(dy + (int64_t)m0 * N);
+    c.ybytes = (uint32_t)((int64_t)mrows * N * 2 > 0x7fffffffll ? 0x7fffffffll : (int64_t)mrows * N * 2);
     c.cr = dx_rsrc(codes, (int64_t)N * (K >> 1));
     // scales: exactly the meaningful entries (an index at or past the end
     // reads zero); NF4_DQ: the 8-bit codes, and zr the run constants

@@ -19,29 +19,29 @@
 //    once.  The loads of the next positions -- of the same or the next row --
 //    are issued before the current stage is computed, so HBM reads stay in
 //    flight.
-//  * The scale is hoisted out of the inner product: a chunk lies inside one
-//    group, so p = sum x * level is formed first and then acc += s * p
-//    (INT4-asym: acc += s * (p - z * sum x)).
-//  * Levels come from a per-workgroup LDS table indexed by a whole code byte:
-//    an entry holds the two nibbles' levels as a packed 16-bit pair, so one
-//    v_dot2_f32_{f16,bf16} multiplies two weights by two activations into an
-//    fp32 accumulator.  The table is replicated per lane (a lane reads only
-//    its own bank) and a byte's LDS address is one v_perm_b32 (code byte ->
-//    address bits 8..15, lane slot -> bits 0..7).
-//  * Level pairs: INT4 levels are small integers, exact in bf16 and fp16, so
-//    the activations are used as they are.  NF4 levels are taken in fp16; for
-//    bf16 activations with M <= 2 the activations are first converted to
-//    fp16 after an exact power-of-two scaling per 32-value chunk (max |x|
-//    mapped into [2^14, 2^15)), which is lossless over fp16's normal range.
-//    For larger M with bf16 activations NF4 levels are split into bf16 hi +
-//    lo parts (two dot2 per byte).
+//  * Every weight enters the product as the value q4_dequantize writes: the
+//    binary32 product level * scale (NF4: Q[i] * c; INT4-sym: (q - 8) * s;
+//    INT4-asym: q * s + (-z * s), both terms exact), rounded once to the
+//    activation dtype.  The levels come from a per-workgroup LDS table
+//    indexed by a whole code byte: an entry holds the binary32 levels of its
+//    two nibbles, so one 8-byte read, two fma and one packed conversion give
+//    a pair of 16-bit weights.  The table is replicated per 32 lane slots (a
+//    lane reads only its own banks) and a byte's LDS address is one
+//    v_perm_b32 (code byte -> address bits 8..15, lane slot -> bits 3..7).
+//  * Multiply-accumulate on the matrix cores: a lane's 8 weights of one
+//    code dword and its own 8 activations form its share of a
+//    v_mfma_f32_16x16x32 (weights as the first operand, activations as the
+//    second).  Output (n, n) of that product sums the four lanes n, n + 16,
+//    n + 32, n + 48 of the same row position, so the diagonal of the 16 x 16
+//    accumulator holds the row's partial sums (the rest is never read); the
+//    vector ALUs only dequantize.  M = 2 runs one product per activation row.
 //  * Activations: for M = 1 and rows that fit one stage (K <= 4096) each lane
 //    keeps its slices in registers; else, for M <= 2, they are staged once
 //    per workgroup in LDS (rows padded to whole stages with zeros, 16 bytes
 //    of skew per 64-byte chunk so the 16-byte reads of a wave do not collide
-//    in banks); larger M reads them from L2 step by step.
-//  * Lane partial sums are reduced across the wave with DPP; y is rounded
-//    once to the activation dtype.
+//    in banks); larger K reads them from L2 step by step.
+//  * At the end of a row the diagonal entries are summed across the wave
+//    with DPP; y is rounded once to the activation dtype.
 //  * NF4 with double-quantized absmax ("Loading a model in 4-bit", "Where
 //    the accuracy goes"): a chunk's scale is read as its group's 8-bit code
 //    (one byte) and its run's binary32 constant (a dword that the 8 to 32
@@ -51,6 +51,7 @@
 
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
+#include "q4_mfma.hpp"
 
 namespace q4 {
 namespace {
@@ -76,45 +77,65 @@ constexpr int kStageXBytes = kStageChunks * 64;  // activation bytes per row per
 // Where a wave reads its activations from.
 enum XSrc { X_GLOBAL = 0, X_LDS = 1, X_REG = 2 };
 
-// Per-kernel arithmetic choices (see the header comment).
-template <int FMT, int ACT, int XS>
-struct Cfg {
-    // bf16 activations converted to fp16 for NF4 when they are staged
-    static constexpr bool conv_x = level_fmt(FMT) == Q4_NF4 && ACT == Q4_BF16 && XS != X_GLOBAL;
-    // dot2 operand type
-    static constexpr int ct = (ACT == Q4_F16 || conv_x) ? Q4_F16 : Q4_BF16;
-    // NF4 in bf16: hi + lo level parts (two table dwords per byte)
-    static constexpr bool pair = level_fmt(FMT) == Q4_NF4 && ct == Q4_BF16;
-};
+// The byte-indexed level table: entry e (a code byte), lane slot L (0..31)
+// at byte 256 e + 8 L holds the binary32 levels of the byte's low and high
+// nibble.  Lanes L and L + 32 read the same slot, in different halves of
+// the wave's 8-byte read, so no read meets a bank conflict.  It is filled
+// in 16-byte pieces (two slots of one entry): thread t writes pieces t,
+// t + BLOCK, ..., so each store instruction covers consecutive addresses.
+constexpr int kTablePieces = kTableDwords / 4;
 
-__constant__ uint32_t c_parts[3][16] = {
-#define ROW(a) {a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7], a[8], a[9], a[10], a[11], a[12], a[13], a[14], a[15]}
-    ROW(kPairParts.nf4_bf16_hi), ROW(kPairParts.nf4_bf16_lo), ROW(kPairParts.nf4_f16_hi),
-#undef ROW
-};
-
-template <int CT>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+// Binary32 level of nibble i: the NF4 table entry, i - 8 (INT4-sym, offset
+// binary) or i (INT4-asym, whose zero-point enters as the bias -z * s).
+// NF4 entries come from a per-lane constant (lane i % 16 holds entry i,
+// built from immediates) by lane permute, so filling the table issues no
+// memory load (which would queue behind the weight loads in flight).
+template <int FMT>
+__device__ __forceinline__ float nf4_lane_entry()
 {
-    if constexpr (CT == Q4_BF16)
-        return __builtin_amdgcn_fdot2_f32_bf16(std::bit_cast<bf16x2>(a), std::bit_cast<bf16x2>(b), c,
-                                               false);
+    const int i = threadIdx.x & 15;
+    float v = kNF4[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k)
+        v = i == k ? kNF4[k] : v;
+    return v;
+}
+template <int FMT>
+__device__ __forceinline__ float level_of(int i, float lane_entry)
+{
+    if constexpr (level_fmt(FMT) == Q4_NF4)
+        return std::bit_cast<float>(__shfl(std::bit_cast<int>(lane_entry), i, 16));
     else
-        return __builtin_amdgcn_fdot2(std::bit_cast<f16x2>(a), std::bit_cast<f16x2>(b), c, false);
+        return (float)(FMT == Q4_INT4_SYM ? i - 8 : i);
 }
 
-template <int CT>
-__device__ __forceinline__ uint32_t level_bits(int v)
+// Fill the table: `block` threads, thread t writes pieces t, t + block, ...
+template <int FMT, int BLOCK>
+__device__ __forceinline__ void fill_level_table(uint32_t *tbl)
 {
-    return CT == Q4_BF16 ? f2bf_bits((float)v) : f2h_bits((float)v);
+    static_assert(kTablePieces % BLOCK == 0, "whole rounds of pieces");
+    const float mine = level_fmt(FMT) == Q4_NF4 ? nf4_lane_entry<FMT>() : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTablePieces / BLOCK; ++i) {
+        const int piece = threadIdx.x + BLOCK * i;
+        const int e = piece >> 4;  // 16 pieces of 16 bytes per 256-byte entry
+        const uint32_t lo = std::bit_cast<uint32_t>(level_of<FMT>(e & 15, mine));
+        const uint32_t hi = std::bit_cast<uint32_t>(level_of<FMT>(e >> 4, mine));
+        ((u32x4 *)tbl)[piece] = u32x4{lo, hi, lo, hi};
+    }
 }
 
-// The byte-indexed table.  Single layout: entry e, lane slot L (0..63) at
-// byte e*256 + 4L.  Pair layout (NF4 in bf16): hi part at e*256 + 4L, lo
-// part at e*256 + 128 + 4L, L in 0..31.  It is filled in 16-byte pieces:
-// thread t writes pieces t, t + BLOCK, ..., so each store instruction covers
-// consecutive addresses; a piece lies in one entry (half), so its dwords
-// are equal.
+// Scale and bias of a chunk's group: weight = fma(level, s, b).  The bias
+// is -0 where there is no zero-point, so fma(level, s, -0) is the plain
+// product level * s (sign of zero included).
+template <int FMT>
+__device__ __forceinline__ float chunk_bias(float s, float zf)
+{
+    if constexpr (FMT == Q4_INT4_ASYM)
+        return -(zf * s);  // exact: z <= 15 and s has 11 significant bits
+    else
+        return -0.0f;
+}
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_f32(float x)
@@ -279,56 +300,34 @@ __device__ __forceinline__ void load_x(u32x4 (&xv)[MT], const uint32_t *xs,
     }
 }
 
-// Largest |value| of the two bf16 halves of a dword.
-__device__ __forceinline__ float bf2_absmax(uint32_t u)
+// Sum of the diagonal of a lane-own-dot 16 x 16 accumulator: entry (n, n)
+// is register n % 4 of lane n + 16 (n / 4), i.e. of the lanes whose
+// position in their 16-lane row is in quad (lane / 16).  Every lane gets
+// the total.
+__device__ __forceinline__ float diag_sum(const f32x4 &a, int lane)
 {
-    return fmaxf(fabsf(std::bit_cast<float>(u << 16)), fabsf(std::bit_cast<float>(u & 0xffff0000u)));
-}
-
-// Maximum over aligned groups of 4 lanes (returned to each lane of the group).
-__device__ __forceinline__ float max4(float v)
-{
-    v = fmaxf(v, dpp_f32<0xb1, 0xf>(v));  // lane ^ 1
-    v = fmaxf(v, dpp_f32<0x4e, 0xf>(v));  // lane ^ 2
-    return v;
-}
-
-// Powers of two f = 2^(14 - e) and 1/f, e the exponent of a >= 0, so that
-// a * f lies in [2^14, 2^15) (clamped so both stay normal binary32).
-__device__ __forceinline__ void x_scale(float a, float &f, float &inv)
-{
-    const uint32_t b = std::bit_cast<uint32_t>(a);
-    int e = b ? (int)((b >> 23) & 0xff) - 127 : 14;
-    e = e < -100 ? -100 : e;
-    f = std::bit_cast<float>((uint32_t)(14 - e + 127) << 23);
-    inv = std::bit_cast<float>((uint32_t)(e - 14 + 127) << 23);
-}
-
-// bf16 pair -> fp16 pair after multiplying by the power of two f (exact over
-// fp16's normal range, nearest-even below it).
-__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t u, float f)
-{
-    const float a = std::bit_cast<float>(u << 16) * f;
-    const float b = std::bit_cast<float>(u & 0xffff0000u) * f;
-    return pack_h2(a, b);
+    const int r = lane & 3;
+    float d = r == 0 ? a[0] : (r == 1 ? a[1] : (r == 2 ? a[2] : a[3]));
+    d = ((lane & 15) >> 2) == (lane >> 4) ? d : 0.0f;
+    return wave_sum(d);
 }
 
 // Products of one stage: 8 steps of 8 weights (two chunks x four dwords of
-// codes).  Scheduling barriers every Q4_GEMV_SB steps keep the table reads of
-// later steps from being hoisted (which would exhaust the register budget).
-template <int FMT, int CT, bool PAIR, int MT, int XS>
-__device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
+// codes).  Per code byte: its LDS address by one v_perm, one 8-byte table
+// read (the two nibbles' binary32 levels), two fma with the chunk's scale
+// and bias and one packed conversion to the activation dtype; per dword one
+// matrix-core product per activation row.  Scheduling barriers every
+// Q4_GEMV_SB steps keep the table reads of later steps from being hoisted
+// (which would exhaust the register budget).
+template <int FMT, int ACT, int MT, int XS>
+__device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
                                               const uint32_t *__restrict__ tbl, const uint32_t *xs,
                                               const u32x4 (&xreg)[XS == X_REG ? 8 * MT : 1],
-                                              const float (&xinv)[MT][2], __amdgpu_buffer_rsrc_t xr,
-                                              int K, int xrow, int s, int lane, int C,
-                                              uint32_t laneoff, int gshift)
+                                              __amdgpu_buffer_rsrc_t xr, int K, int xrow, int s,
+                                              int lane, int C, uint32_t laneoff, int gshift)
 {
     constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
-    const uint32_t ones = CT == Q4_BF16 ? 0x3f803f80u : 0x3c003c00u;
-    // two independent accumulator chains per output (and two more for the lo
-    // parts), so consecutive dot2 do not wait on each other
-    constexpr int NA = MT <= 2 ? 2 : 1;
+    constexpr bool nf4 = level_fmt(FMT) == Q4_NF4;
     u32x4 xv[MT];
     if constexpr (XS == X_REG) {
 #pragma unroll
@@ -339,15 +338,32 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float p[MT][NA], pl[MT][NA];
-        float sx[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            sx[m] = 0.0f;
-#pragma unroll
-            for (int a = 0; a < NA; ++a)
-                p[m][a] = pl[m][a] = 0.0f;
+        float sc = st.sc[h];
+        if constexpr (FMT == Q4_NF4_DQ) {
+            // The half's 64 chunks cover at most 64 groups, so at most
+            // two runs: the run of its first group (ra) and the next
+            // (rb), picked per half from wave-uniform values; a lane
+            // takes rb when its group is at or past the run boundary.
+            // Groups are counted from the start of the row's first run.
+            const int u = st.zpar + ((kStageChunks * 32 * s + 64 * 32 * h) >> gshift);
+            const int r0 = u >> 8;                         // 0..2
+            const int thr = 256 * (r0 + 1) - u;            // first lane group in rb
+            const uint32_t a0 = std::bit_cast<uint32_t>(st.s2[0]);
+            const uint32_t a1 = std::bit_cast<uint32_t>(st.s2[1]);
+            const uint32_t a2 = std::bit_cast<uint32_t>(st.s2[2]);
+            const uint32_t ra = r0 == 0 ? a0 : (r0 == 1 ? a1 : a2);
+            const uint32_t rb = r0 == 0 ? a1 : a2;
+            const int lg = (32 * lane) >> gshift;          // the lane's group in the half
+            const float s2 = std::bit_cast<float>(lg >= thr ? rb : ra);
+            // c' = qc * s2.  A chunk past the row end has qc = 0 (its load
+            // is out of the view) and its run may lie past the last one,
+            // where the constant is read from the buffer's padding (any
+            // bits): c' = 0 there without the product.  For a real group
+            // with qc = 0 this is the same +0 as the product.
+            const uint32_t qc = std::bit_cast<uint32_t>(st.sc[h]);
+            sc = qc != 0 ? keep_f32((float)qc * s2) : 0.0f;
         }
+        const float bias = chunk_bias<FMT>(sc, st.zf[h]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             u32x4 xn[MT];
@@ -361,27 +377,24 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
                                    C, (j + 1) & 3);
                 }
             }
-            if constexpr (FMT == Q4_INT4_ASYM) {
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        sx[m] = dot2<CT>(xv[m][k], ones, sx[m]);
-            }
+            u32x4 wf;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t addr = __builtin_amdgcn_perm(st.cw[h][j], laneoff, kSel[k]);
-                const uint32_t lv = *(const uint32_t *)((const char *)tbl + addr);
-                uint32_t lo = 0;
-                if constexpr (PAIR)
-                    lo = *(const uint32_t *)((const char *)tbl + addr + 128);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    p[m][k % NA] = dot2<CT>(xv[m][k], lv, p[m][k % NA]);
-                    if constexpr (PAIR)
-                        pl[m][k % NA] = dot2<CT>(xv[m][k], lo, pl[m][k % NA]);
+                const float2 lv = *(const float2 *)((const char *)tbl + addr);
+                float w0 = __builtin_fmaf(lv.x, sc, bias);
+                float w1 = __builtin_fmaf(lv.y, sc, bias);
+                if constexpr (nf4) {
+                    // rounded to binary32 first, then to the activation
+                    // dtype (no single-rounding mixed fma)
+                    w0 = keep_f32(w0);
+                    w1 = keep_f32(w1);
                 }
+                wf[k] = ACT == Q4_BF16 ? pack_bf2(w0, w1) : pack_h2(w0, w1);
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[m] = mfma<ACT>(wf, xv[m], acc[m]);
             if (h * 4 + j < 7) {
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
@@ -391,35 +404,6 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float (&acc)[MT],
             if ((j + 1) % Q4_GEMV_SB == 0)
                 __builtin_amdgcn_sched_barrier(0);
 #endif
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            float t = 0.0f;
-#pragma unroll
-            for (int a = 0; a < NA; ++a)
-                t += PAIR ? p[m][a] + pl[m][a] : p[m][a];
-            if constexpr (FMT == Q4_INT4_ASYM)
-                t = __builtin_fmaf(-st.zf[h], sx[m], t);
-            float sc = st.sc[h];
-            if constexpr (FMT == Q4_NF4_DQ) {
-                // The half's 64 chunks cover at most 64 groups, so at most
-                // two runs: the run of its first group (ra) and the next
-                // (rb), picked per half from wave-uniform values; a lane
-                // takes rb when its group is at or past the run boundary.
-                // Groups are counted from the start of the row's first run.
-                const int u = st.zpar + ((kStageChunks * 32 * s + 64 * 32 * h) >> gshift);
-                const int r0 = u >> 8;                         // 0..2
-                const int thr = 256 * (r0 + 1) - u;            // first lane group in rb
-                const uint32_t a0 = std::bit_cast<uint32_t>(st.s2[0]);
-                const uint32_t a1 = std::bit_cast<uint32_t>(st.s2[1]);
-                const uint32_t a2 = std::bit_cast<uint32_t>(st.s2[2]);
-                const uint32_t ra = r0 == 0 ? a0 : (r0 == 1 ? a1 : a2);
-                const uint32_t rb = r0 == 0 ? a1 : a2;
-                const int lg = (32 * lane) >> gshift;          // the lane's group in the half
-                const float s2 = std::bit_cast<float>(lg >= thr ? rb : ra);
-                sc = keep_f32((float)std::bit_cast<uint32_t>(st.sc[h]) * s2);  // c' = qc * s2
-            }
-            acc[m] = __builtin_fmaf(t, sc * xinv[m][h], acc[m]);
         }
     }
 }
@@ -456,7 +440,6 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                  const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K,
                  int gshift, uint16_t *__restrict__ y)
 {
-    using F = Cfg<FMT, ACT, XS>;
     constexpr int kWaves = Shape<XS>::waves;
     constexpr int kBlock = Shape<XS>::block;
     // One LDS block with the table first, at address 0, so that a lookup's
@@ -464,16 +447,13 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     struct Lds {
         uint32_t tbl[kTableDwords];
         uint32_t xs[XS != X_GLOBAL ? kXBytes / 4 : 4];
-        // inverse activation scale of each staged 32-value chunk
-        float xsinv[XS != X_GLOBAL && Cfg<FMT, ACT, XS>::conv_x ? kXBytes / 64 : 1];
     };
     __shared__ Lds lds;
     uint32_t *const tbl = lds.tbl;
     uint32_t *const xs = lds.xs;
-    float *const xsinv = lds.xsinv;
 
     const int lane = threadIdx.x & 63;
-    const uint32_t laneoff = (uint32_t)(F::pair ? (lane & 31) : lane) << 2;
+    const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const int C = K >> 5;                                    // 16-byte chunks per row
     const int S = (C + kStageChunks - 1) / kStageChunks;    // stages per row
     const int G = K >> gshift;                               // groups per row
@@ -492,7 +472,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 
     // Prologue, ordered so that nothing waits behind the weight stream
     // (vector-memory loads retire in order): activations first, then the
-    // table's level values, then the first P weight positions.
+    // first P weight positions, then the table.
     u32x4 xreg[XS == X_REG ? 8 * MT : 1];
     constexpr int XP = Shape<XS>::x_pieces;
     u32x4 xt[XP];
@@ -510,13 +490,6 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 xt[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, m * 2 * K + o, 0, 0);
         }
     }
-    // NF4 level parts: lane i (mod 16) holds entry i; fetched by lane permutes
-    uint32_t part_lo = 0, part_hi = 0;
-    if constexpr (level_fmt(FMT) == Q4_NF4) {
-        part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
-        if constexpr (F::pair)
-            part_hi = c_parts[1][lane & 15];
-    }
 
     // ring of P in-flight positions (a row past the end has an empty view,
     // so its loads return zeros and it is never computed)
@@ -531,66 +504,17 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
         load_stage<FMT>(st[q], v, pos[q].s, lane, gshift, C);
     }
 
-    // fp16 conversion of bf16 activations with a power-of-two scale per
-    // 32-value chunk (half of a lane's share of a stage); the products are
-    // scaled back exactly together with the group scale
+    fill_level_table<FMT, kBlock>(tbl);
     if constexpr (XS != X_GLOBAL) {
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            if constexpr (F::conv_x) {
-                // the 4 pieces of a chunk sit in 4 consecutive threads
-                float mx = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    mx = fmaxf(mx, bf2_absmax(xt[i][k]));
-                mx = max4(mx);
-                float f, inv;
-                x_scale(mx, f, inv);
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    xt[i][k] = bf2_to_h2(xt[i][k], f);
-                if (xp[i] >= 0 && (xp[i] & 3) == 0)
-                    xsinv[xp[i] >> 2] = inv;
-            }
+        for (int i = 0; i < XP; ++i)
             if (xp[i] >= 0)
                 *(u32x4 *)((char *)xs + xpad(16 * xp[i])) = xt[i];
-        }
-    }
-    // table: level values by lane permutes (NF4) or arithmetic (INT4)
-#pragma unroll
-    for (int i = 0; i < kTableDwords / 4 / kBlock; ++i) {
-        const int piece = threadIdx.x + kBlock * i;
-        const int e = piece >> 4, h = (piece >> 3) & 1;
-        const int n0 = e & 15, n1 = e >> 4;
-        uint32_t v;
-        if constexpr (level_fmt(FMT) == Q4_NF4) {
-            // every lane holds the same part variable, so the permute reads
-            // entry n of that part; the hi/lo choice is made afterwards
-            uint32_t a = (uint32_t)__shfl((int)part_lo, n0), b = (uint32_t)__shfl((int)part_lo, n1);
-            if constexpr (F::pair) {
-                const uint32_t c = (uint32_t)__shfl((int)part_hi, n0);
-                const uint32_t d = (uint32_t)__shfl((int)part_hi, n1);
-                if (h) {
-                    a = c;
-                    b = d;
-                }
-            }
-            v = a | (b << 16);
-        } else {
-            const int off = FMT == Q4_INT4_SYM ? 8 : 0;
-            v = level_bits<F::ct>(n0 - off) | (level_bits<F::ct>(n1 - off) << 16);
-        }
-        ((u32x4 *)tbl)[piece] = u32x4{v, v, v, v};
     }
     __syncthreads();
 
     // one stage per row (M = 1): each lane keeps its activation slices
-    // (chunks lane and 64 + lane) and their inverse scales in registers for
-    // the whole kernel
-    float xinv_reg[MT][2];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        xinv_reg[m][0] = xinv_reg[m][1] = 1.0f;
+    // (chunks lane and 64 + lane) in registers for the whole kernel
     if constexpr (XS == X_REG) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -599,17 +523,13 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 xreg[m * 8 + t] = *(const u32x4 *)((const char *)xs +
                                                    xpad(m * xrow + 64 * stage_chunk(0, lane, t >> 2) +
                                                         16 * (t & 3)));
-            if constexpr (F::conv_x) {
-                xinv_reg[m][0] = xsinv[m * (xrow >> 6) + stage_chunk(0, lane, 0)];
-                xinv_reg[m][1] = xsinv[m * (xrow >> 6) + stage_chunk(0, lane, 1)];
-            }
         }
     }
 
-    float acc[MT];
+    f32x4 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-        acc[m] = 0.0f;
+        acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // A round of the ring is never left in the middle (the load waits stay
     // partial only if every path refills every slot): a position past the
@@ -619,19 +539,8 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const Pos cp = pos[q];
-            float xinv[MT][2];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if constexpr (F::conv_x && XS == X_LDS)
-                        xinv[m][h] = xsinv[m * (xrow >> 6) + stage_chunk(cp.s, lane, h)];
-                    else
-                        xinv[m][h] = xinv_reg[m][h];
-                }
-            }
-            compute_stage<FMT, F::ct, F::pair, MT, XS>(st[q], acc, tbl, xs, xreg, xinv, xr, K,
-                                                      xrow, cp.s, lane, C, laneoff, gshift);
+            compute_stage<FMT, ACT, MT, XS>(st[q], acc, tbl, xs, xreg, xr, K, xrow, cp.s, lane, C,
+                                           laneoff, gshift);
             // (double quantization: keep the refill after the compute, which
             // the scheduler otherwise hoists at the cost of registers)
             if constexpr (FMT == Q4_NF4_DQ)
@@ -647,8 +556,8 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 float out = 0.0f;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const float t = wave_sum(acc[m]);
-                    acc[m] = 0.0f;
+                    const float t = diag_sum(acc[m], lane);
+                    acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                     if (lane == m)
                         out = t;
                 }
@@ -754,6 +663,10 @@ __device__ __forceinline__ TaskViews task_views(const ChainTask &T, int gshift)
 
 // The loads of stage s of row `row` (row == N: past the last row, every load
 // is out of the views and returns zero), as load_stage does with row views.
+// The row's and the stage's place is added to the lane's offset (voffset),
+// which the buffer unit range-checks against the view (a load's soffset is
+// not checked), so a position past the last row or a chunk past the row
+// end reads zeros and never touches memory outside the task's arrays.
 template <int FMT>
 __device__ __forceinline__ void load_stage_chain(Stage &st, const TaskViews &tv, int row, int s,
                                                  int lane, int gshift)
@@ -761,30 +674,31 @@ __device__ __forceinline__ void load_stage_chain(Stage &st, const TaskViews &tv,
     constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     const int g0 = row * tv.G;                                // the row's first flat group
     const int gs = (kStageChunks * 32 * s) >> gshift;          // the stage's first group in the row
-    const int cd_off = row * tv.row_bytes + 16 * kStageChunks * s;
-    const int sc_off = (g0 + gs) * ss;
+    const uint32_t cd_off = (uint32_t)(row * tv.row_bytes + 16 * kStageChunks * s);
+    const uint32_t sc_off = (uint32_t)((g0 + gs) * ss);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int lc = 64 * h + lane;                         // chunk within the stage
         const bool in = kStageChunks * s + lc < tv.C;
-        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(tv.codes, in ? 16 * lc : kChainOob, cd_off,
-                                                         kNT);
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(tv.codes, in ? cd_off + 16 * lc : kChainOob,
+                                                         0, kNT);
         const int gl = (32 * lc) >> gshift;                    // group within the stage
         if constexpr (FMT == Q4_NF4)
-            st.sc[h] = std::bit_cast<float>(
-                __builtin_amdgcn_raw_buffer_load_b32(tv.scales, in ? 4 * gl : kChainOob, sc_off, kNT));
+            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(
+                tv.scales, in ? sc_off + 4 * gl : kChainOob, 0, kNT));
         else if constexpr (FMT == Q4_NF4_DQ)
             st.sc[h] = std::bit_cast<float>((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-                tv.scales, in ? gl : kChainOob, sc_off, kNT));
+                tv.scales, in ? sc_off + gl : kChainOob, 0, kNT));
         else
-            st.sc[h] = h2f(
-                __builtin_amdgcn_raw_buffer_load_b16(tv.scales, in ? 2 * gl : kChainOob, sc_off, kNT));
+            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(
+                tv.scales, in ? sc_off + 2 * gl : kChainOob, 0, kNT));
         if constexpr (FMT == Q4_INT4_ASYM) {
             // nibble g0 + gs + gl; gs is even, so the byte is
             // (g0 >> 1) + gs / 2 + ((g0 & 1) + gl) / 2
             const int gz = (g0 & 1) + gl;
+            const uint32_t z_off = (uint32_t)((g0 >> 1) + (gs >> 1));
             const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
-                tv.zeros, in ? gz >> 1 : kChainOob, (g0 >> 1) + (gs >> 1), kNT);
+                tv.zeros, in ? z_off + (gz >> 1) : kChainOob, 0, kNT);
             st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
         } else {
             st.zf[h] = 0.0f;
@@ -814,16 +728,14 @@ __device__ __forceinline__ void wait_vm()
 // x of a chained task in LDS: stage s in slot (base + s) mod 8, piece-major
 // within the stage (piece j of its local chunk c at 16-byte index
 // 128 j + c of the slot), so that the 16 lanes of a read pass take 256
-// consecutive bytes (no bank conflicts); the inverse scales of stage s at
-// float index 128 slot + c.
+// consecutive bytes (no bank conflicts).
 __device__ __forceinline__ int chain_slot(int base, int s) { return (base + s) & (kChainSlots - 1); }
 __device__ __forceinline__ int chain_x_index(int slot, int j, int c) { return 512 * slot + 128 * j + c; }
 
 // A lane's x slice for stage s of a row: chunks l and 64 + l of the stage
-// (the stored rows are zero past K up to whole stages), with the inverse
-// scales of their conversion.
-__device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2], const u32x4 *xb,
-                                              const float *inv, int base, int s, int lane)
+// (the stored rows are zero past K up to whole stages).
+__device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], const u32x4 *xb, int base, int s,
+                                              int lane)
 {
     const int slot = chain_slot(base, s);
 #pragma unroll
@@ -831,7 +743,6 @@ __device__ __forceinline__ void chain_x_slice(u32x4 (&xreg)[8], float (&xinv)[2]
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             xreg[4 * h + j] = xb[chain_x_index(slot, j, 64 * h + lane)];
-        xinv[h] = inv[kStageChunks * slot + 64 * h + lane];
     }
 }
 
@@ -860,7 +771,9 @@ constexpr int kChainDmaAhead = 40;
 // several tasks in flight): per stage, half and piece, one 16-byte load per
 // lane, lane l's piece j of chunk c0 + l landing at 16-byte index
 // 128 j + c0 + l of the slot, the piece-major order the compute waves read.
-// Chunks past K read zeros: the stored rows are padded to whole stages.
+// The whole offset is the lane's (voffset, range-checked against the x
+// view), so pieces past K read zeros: the stored rows are padded to whole
+// stages with zeros.
 __device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int lane)
 {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
@@ -874,49 +787,7 @@ __device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int l
             for (int j = 0; j < 4; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xr, (__attribute__((address_space(3))) void *)(xb + chain_x_index(slot, j, 64 * h)),
-                    16, 64 * lane, 64 * (kStageChunks * s + 64 * h) + 16 * j, 0, 0);
-    }
-}
-
-// Once a task's x is in its slots: converted in place where the arithmetic
-// uses fp16 for bf16 activations (per 32-value chunk, max |x| scaled into
-// [2^14, 2^15) by a power of two: the staged single-product conversion);
-// inv receives the chunks' inverse scales (1 when nothing is converted).
-template <int FMT, int ACT>
-__device__ __forceinline__ void chain_convert_x(const ChainTask &T, u32x4 *xb, float *inv, int lane)
-{
-    using F = Cfg<FMT, ACT, X_LDS>;
-    const int S = chain_stages(T.K);
-    const int base = ctl_base(T.ctl);
-    for (int s = 0; s < S; ++s) {
-        const int slot = chain_slot(base, s);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 64 * h + lane;
-            float iv = 1.0f;
-            if constexpr (F::conv_x) {
-                u32x4 v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[j] = xb[chain_x_index(slot, j, c)];
-                float mx = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        mx = fmaxf(mx, bf2_absmax(v[j][k]));
-                float f;
-                x_scale(mx, f, iv);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        v[j][k] = bf2_to_h2(v[j][k], f);
-                    xb[chain_x_index(slot, j, c)] = v[j];
-                }
-            }
-            inv[kStageChunks * slot + c] = iv;
-        }
+                    16, 64 * (kStageChunks * s + 64 * h + lane) + 16 * j, 0, 0, 0);
     }
 }
 
@@ -947,15 +818,11 @@ template <int FMT, int ACT, int P, bool DEP>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void gemv_chain_kernel(const ChainArgs a)
 {
-    using F = Cfg<FMT, ACT, X_LDS>;  // the arithmetic of the staged single-product kernels
-    static_assert(Cfg<FMT, ACT, X_REG>::ct == F::ct && Cfg<FMT, ACT, X_REG>::pair == F::pair,
-                  "x source must not change the arithmetic");
     // One LDS block with the table first, at address 0, so that a lookup's
     // address is the v_perm result itself.
     struct Lds {
         uint32_t tbl[kTableDwords];
         u32x4 xb[kChainSlots * 512];
-        float xinv[kChainSlots * kStageChunks];
         int entered[kChainMax];  // compute waves that entered each task
         int ready[kChainMax];    // 1 once x of the task is in its slots
         ChainTask tasks[kChainMax];
@@ -963,13 +830,12 @@ void gemv_chain_kernel(const ChainArgs a)
     __shared__ Lds lds;
     uint32_t *const tbl = lds.tbl;
     auto &xb = lds.xb;
-    auto &xinv_lds = lds.xinv;
     auto &entered = lds.entered;
     auto &ready = lds.ready;
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t laneoff = (uint32_t)(F::pair ? (lane & 31) : lane) << 2;
+    const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const int nt = a.ntasks;
     // every compute wave has entered task t
     auto all_entered = [&](int t) {
@@ -979,37 +845,7 @@ void gemv_chain_kernel(const ChainArgs a)
     auto fail = [&]() { __hip_atomic_store(&a.sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 
     // the level table, by every wave
-    {
-        uint32_t part_lo = 0, part_hi = 0;
-        if constexpr (level_fmt(FMT) == Q4_NF4) {
-            part_lo = c_parts[F::pair ? 0 : 2][lane & 15];
-            if constexpr (F::pair)
-                part_hi = c_parts[1][lane & 15];
-        }
-#pragma unroll
-        for (int i = 0; i < kTableDwords / 4 / 1024; ++i) {
-            const int piece = threadIdx.x + 1024 * i;
-            const int e = piece >> 4, h = (piece >> 3) & 1;
-            const int n0 = e & 15, n1 = e >> 4;
-            uint32_t v;
-            if constexpr (level_fmt(FMT) == Q4_NF4) {
-                uint32_t x0 = (uint32_t)__shfl((int)part_lo, n0), x1 = (uint32_t)__shfl((int)part_lo, n1);
-                if constexpr (F::pair) {
-                    const uint32_t c0 = (uint32_t)__shfl((int)part_hi, n0);
-                    const uint32_t c1 = (uint32_t)__shfl((int)part_hi, n1);
-                    if (h) {
-                        x0 = c0;
-                        x1 = c1;
-                    }
-                }
-                v = x0 | (x1 << 16);
-            } else {
-                const int off = FMT == Q4_INT4_SYM ? 8 : 0;
-                v = level_bits<F::ct>(n0 - off) | (level_bits<F::ct>(n1 - off) << 16);
-            }
-            ((u32x4 *)tbl)[piece] = u32x4{v, v, v, v};
-        }
-    }
+    fill_level_table<FMT, 1024>(tbl);
     // the task table into LDS, read there at every task switch: through the
     // scalar cache, a miss would stall the wave (and the loads of its next
     // rows) for a loaded memory system's latency once per task
@@ -1074,7 +910,7 @@ void gemv_chain_kernel(const ChainArgs a)
         // x goes in by DMA as early as the slots allow: a later task's as
         // soon as its gate is open (unless it reads earlier outputs), up to
         // kChainDmaAhead instructions ahead; the current task's is then
-        // awaited, converted and published.
+        // awaited and published.
         int issued = 0;  // tasks whose x DMA is issued (in order)
         int ahead = 0;   // DMA instructions in flight for tasks after the current one
         auto dma_count = [&](const ChainTask &T) { return kChainDmaPerStage * chain_stages(T.K); };
@@ -1091,8 +927,6 @@ void gemv_chain_kernel(const ChainArgs a)
         };
         auto publish = [&](int t) {
             wait_vm_upto(ahead);  // task t's DMA is done (they complete in order)
-            chain_convert_x<FMT, ACT>(task(t), xb, xinv_lds, lane);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): x is in LDS
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __hip_atomic_store(&ready[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
@@ -1276,9 +1110,8 @@ void gemv_chain_kernel(const ChainArgs a)
         // past the last task has loaded zeros from an empty view; it is
         // computed on them and writes nothing.
         u32x4 xreg[8];
-        float xinv_reg[2] = {1.0f, 1.0f};
         int xkey = -1;
-        float acc[1] = {0.0f};
+        f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
         while (pos[0].t < nt) {
 #pragma unroll
             for (int q = 0; q < P; ++q) {
@@ -1290,17 +1123,16 @@ void gemv_chain_kernel(const ChainArgs a)
                 }
                 const int key = 8 * cp.t + cp.s;
                 if (key != xkey) {
-                    chain_x_slice(xreg, xinv_reg, xb, xinv_lds, cp.xbase, cp.s, lane);
+                    chain_x_slice(xreg, xb, cp.xbase, cp.s, lane);
                     xkey = key;
                 }
-                const float xinv[1][2] = {{xinv_reg[0], xinv_reg[1]}};
                 // (x comes from registers: no x view, K or chunk count needed)
-                compute_stage<FMT, F::ct, F::pair, 1, X_REG>(st[q], acc, tbl, nullptr, xreg, xinv,
-                                                           make_rsrc(nullptr, 0), 0, 0, cp.s, lane,
-                                                           0, laneoff, a.gshift);
+                compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
+                                                  make_rsrc(nullptr, 0), 0, 0, cp.s, lane, 0,
+                                                  laneoff, a.gshift);
                 if (cp.last) {
-                    const float out = wave_sum(acc[0]);
-                    acc[0] = 0.0f;
+                    const float out = diag_sum(acc[0], lane);
+                    acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                     if (live && lane == 0)
                         // through a global (not flat) pointer: a flat store may
                         // write LDS, so LDS reads after it would wait for it

@@ -145,7 +145,7 @@ q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
     q4_status st = check_product(f, g, act_t, x, M, codes, scales, zeros, N, K, y);
     if (st != Q4_OK)
         return st;
-    if (M > 16)
+    if (M > 16 || K > Q4_GEMV_MAX_K)
         return Q4_EUNSUPPORTED;
     return from_hip(q4::launch_gemv(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                     (hipStream_t)stream));
@@ -184,17 +184,15 @@ q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t
                                        (hipStream_t)stream));
 }
 
-q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
-                        int ntasks, uint32_t *sync, void *stream)
+static q4_status check_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                             int ntasks)
 {
     if (!format_ok(f) || !group_ok(g) || !dtype_ok(act_t))
         return Q4_EUNSUPPORTED;
-    if (!tasks || !sync || ntasks <= 0)
+    if (!tasks || ntasks <= 0)
         return Q4_EINVAL;
     if (ntasks > Q4_GEMV_CHAIN_MAX)
         return Q4_EUNSUPPORTED;
-    if (!aligned(sync, 16))
-        return Q4_EALIGN;
     for (int i = 0; i < ntasks; ++i) {
         const q4_gemv_task &t = tasks[i];
         q4_status st = check_product(f, g, act_t, t.x, 1, t.codes, t.scales, t.zeros, t.N, t.K,
@@ -208,6 +206,19 @@ q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *
         if (t.N * (t.K / 2) > Q4_GEMV_CHAIN_MAX_CODES)  // 32-bit offsets into one view
             return Q4_EUNSUPPORTED;
     }
+    return Q4_OK;
+}
+
+q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                        int ntasks, uint32_t *sync, void *stream)
+{
+    if (!sync && format_ok(f) && group_ok(g) && dtype_ok(act_t))
+        return Q4_EINVAL;
+    q4_status st = check_chain(f, g, act_t, tasks, ntasks);
+    if (st != Q4_OK)
+        return st;
+    if (!aligned(sync, 16))
+        return Q4_EALIGN;
     return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
 }
 

@@ -160,32 +160,6 @@ static_assert(kNF4Buckets.min_edge_distance > 1.0f / 64, "threshold too close to
 static_assert(kNF4Buckets.e[32].base == 15, "x = 1 must code to 15");
 static_assert(kNF4Buckets.e[0].base == 0, "x = -1 must code to 0");
 
-// Pair tables for the GEMV: the entry of a code byte holds the levels of its
-// two nibbles (low nibble in the low half) as a 16-bit pair, so one dot2
-// instruction multiplies two weights by two activations.  NF4 levels are not
-// exact in 16 bits, so they are split into hi + lo 16-bit parts.
-struct PairTables {
-    uint32_t nf4_bf16_hi[16], nf4_bf16_lo[16];
-    uint32_t nf4_f16_hi[16], nf4_f16_lo[16];
-};
-constexpr PairTables make_pair_parts()
-{
-    PairTables p{};
-    for (int i = 0; i < 16; ++i) {
-        float q = kNF4[i];
-        uint16_t bh = bf16_rne_bits(q);
-        uint16_t bl = bf16_rne_bits(q - bf16_bits_f32(bh));
-        uint16_t hh = f16_rne_bits(q);
-        uint16_t hl = f16_rne_bits(q - f16_bits_f32(hh));
-        p.nf4_bf16_hi[i] = bh;
-        p.nf4_bf16_lo[i] = bl;
-        p.nf4_f16_hi[i] = hh;
-        p.nf4_f16_lo[i] = hl;
-    }
-    return p;
-}
-inline constexpr PairTables kPairParts = make_pair_parts();
-
 // --------------------------------------------------------------------------
 // Device helpers.
 __device__ __forceinline__ float h2f(uint32_t bits16)

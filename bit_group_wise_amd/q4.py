@@ -253,12 +253,9 @@ def chain_sync(device):
     return torch.zeros((CHAIN_SYNC_BYTES // 4,), dtype=torch.int32, device=device)
 
 
-def gemv_chain(tasks, sync=None):
-    """Run M = 1 GEMVs in order in one launch (q4_gemv_chain).
-
-    tasks: sequence of (x [1, K], QuantizedWeight, y [1, N] or None[, flags]);
-    every weight shares one format and group size, every x one dtype.
-    Returns the list of outputs."""
+def _chain_tasks(tasks):
+    """The q4_gemv_task array of a chain, its outputs, format, group size
+    and activation code."""
     torch = _torch()
     if not tasks:
         raise ValueError("empty chain")
@@ -280,10 +277,20 @@ def gemv_chain(tasks, sync=None):
         arr[i] = GemvTask(_ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.zeros), _ptr(y),
                           q.N, q.K, flags)
         outs.append(y)
+    return arr, outs, q0.fmt, q0.g, act
+
+
+def gemv_chain(tasks, sync=None):
+    """Run M = 1 GEMVs in order in one launch (q4_gemv_chain).
+
+    tasks: sequence of (x [1, K], QuantizedWeight, y [1, N] or None[, flags]);
+    every weight shares one format and group size, every x one dtype.
+    Returns the list of outputs."""
+    arr, outs, fmt, g, act = _chain_tasks(tasks)
     if sync is None:
         sync = chain_sync(tasks[0][0].device)
     _cuda(sync, "sync")
-    st = lib().q4_gemv_chain(q0.fmt, q0.g, act, ctypes.addressof(arr), len(tasks), _ptr(sync),
+    st = lib().q4_gemv_chain(fmt, g, act, ctypes.addressof(arr), len(tasks), _ptr(sync),
                              _stream_ptr(tasks[0][0]))
     _check(st, "q4_gemv_chain")
     return outs

@@ -98,17 +98,28 @@ typedef enum {
     Q4_EINVAL = 1,       /* null pointer, N/K/M <= 0, K % g != 0, zeros given
                             (or missing) for the format */
     Q4_EUNSUPPORTED = 2, /* unknown format or dtype, g not in {32, 64, 128},
-                            M > 16 for q4_gemv */
+                            M > 16 for q4_gemv, a size beyond an entry
+                            point's stated limit */
     Q4_EALIGN = 3,       /* a pointer violates the alignment rules above */
     Q4_EHIP = 4          /* the HIP runtime refused a launch */
 } q4_status;
 
 /* Sizes in bytes of the caller-allocated buffers for an [N, K] weight with
- * groups of g (0 for invalid arguments).  The scale and zero-point sizes
- * include at least 16 bytes of trailing padding, rounded to a multiple of
- * 16: q4_quantize writes only the leading entries (the padding stays as the
- * caller left it) and no reader uses the padding as values, but q4_gemm's
- * wide loads may read into it, so the whole size must be allocated. */
+ * groups of g (0 for invalid arguments).
+ *   codes:  exactly N*K/2.
+ *   scales: the meaningful size -- N*(K/g)*4 (NF4), N*(K/g)*2 (INT4), or
+ *           for NF4_DQ the 8-bit codes padded to a multiple of 16 plus
+ *           4*ceil(N*(K/g)/256) -- plus P bytes of trailing padding;
+ *   zeros:  the meaningful size ceil(N*(K/g)/2) (INT4-asym; 0 otherwise)
+ *           plus P bytes of trailing padding;
+ * where P = 16 + (the meaningful size rounded up to a multiple of 16, minus
+ * the meaningful size), i.e. the total is the meaningful size plus 16,
+ * rounded up to a multiple of 16.  Every entry point reads the meaningful
+ * bytes only as values; q4_gemm with M > 16 fetches a row's scales and
+ * zero-points for 256 columns at a time with wide loads that may start at
+ * the last meaningful bytes and run into the padding, so a caller must
+ * allocate the padded size (the padding's contents are never used and may
+ * be anything).  q4_quantize writes only the meaningful bytes. */
 size_t q4_codes_bytes(int64_t N, int64_t K);                      /* N*K/2 */
 size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4), padded;
                                                                       NF4_DQ: qc, s2 as above, padded */
@@ -129,11 +140,14 @@ q4_status q4_dequantize(q4_format f, int g, const uint8_t *codes, const void *sc
 
 /* Decode-shape product y[M, N] = x[M, K] . What^T for 1 <= M <= 16, reading
  * the packed weights once and dequantizing them in registers; fp32
- * accumulation, one rounding of y to act_t.  Equal to a 16-bit matmul on the
- * dequantized weights up to rounding order ("Where the accuracy goes").
- * M = 1, 2 run on the vector ALUs; 3 <= M <= 16 as a skinny matrix-core
- * product (weights dequantized to act_t as q4_dequantize writes them).
- * M > 16 returns Q4_EUNSUPPORTED (use q4_gemm). */
+ * accumulation, one rounding of y to act_t.  Every weight enters as the
+ * value q4_dequantize writes in act_t, so the result equals a 16-bit matmul
+ * on the dequantized weights up to summation order ("Where the accuracy
+ * goes").  M = 1, 2 dequantize on the vector ALUs with one row per wave;
+ * 3 <= M <= 16 run as a skinny product over blocks of 16 rows; both
+ * multiply on the matrix cores.  M > 16 returns Q4_EUNSUPPORTED (use
+ * q4_gemm); K > Q4_GEMV_MAX_K returns Q4_EUNSUPPORTED. */
+#define Q4_GEMV_MAX_K 33554432
 q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
                   int64_t N, int64_t K, void *y, void *stream);

@@ -147,6 +147,26 @@ def test_gemv_rejects_m_above_16():
     assert call_gemv(M=17) == q4.EUNSUPPORTED
 
 
+def header_define(name):
+    with open(os.path.join(ROOT, "include", "q4.h")) as f:
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)", f.read())
+    return int(m.group(1))
+
+
+def test_k_limits():
+    """The largest K each product accepts: q4_gemm keeps a 256-row x tile
+    view within 2^31 bytes (its 32-bit buffer range), q4_gemv keeps the
+    skinny product's 16-row offsets within 31 bits.  One group past the limit
+    is rejected before any HIP call."""
+    gemm_k, gemv_k = header_define("Q4_GEMM_MAX_K"), header_define("Q4_GEMV_MAX_K")
+    assert 256 * gemm_k * 2 <= 2**31
+    assert 16 * gemv_k * 2 < 2**31 and 64 * (gemv_k // 2) < 2**31
+    for g in (32, 64, 128):
+        assert call_gemv(name="q4_gemm", M=32, K=gemm_k + g, g=g) == q4.EUNSUPPORTED
+        assert call_gemv(name="q4_gemv", M=1, K=gemv_k + g, g=g) == q4.EUNSUPPORTED
+        assert call_gemv(name="q4_gemv", M=16, K=gemv_k + g, g=g) == q4.EUNSUPPORTED
+
+
 def test_dequantize_rejects():
     L = q4.lib()
     assert L.q4_dequantize(q4.NF4, 64, A, A, None, 4, 128, 5, A, None) == q4.EUNSUPPORTED

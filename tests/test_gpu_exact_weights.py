@@ -1,0 +1,227 @@
+"""Products whose tolerance is only met when every weight enters as the value
+q4_dequantize writes in the activation dtype ("Loading a model in 4-bit",
+"Where the accuracy goes": the layer dequantizes to the 16-bit compute dtype
+and runs an ordinary 16-bit matmul).
+
+An implementation that applies the group scale after the sum (each weight
+then enters as the unrounded binary32 product level * scale) is off by up to
+half an ulp of the activation dtype per term: 2^-8 relative in bf16, above
+the 2e-3 of the tolerance.  The rows here make that gap as large as it gets:
+
+* bf16: dequantized values that sit exactly halfway between two bf16 numbers
+  (level 1 times a scale 1 + (2m + 1) 2^-8, or an NF4 block whose entries
+  all equal its absmax), with x = +-1 chosen by the sign of each weight's
+  rounding, so every term's rounding adds up;
+* fp16: dequantized values in fp16's subnormal range, where the rounding is
+  a large fraction of the value, with x = +-1000 by the same rule.
+
+Each construction first asserts, on the oracle's own numbers, that the gap
+between the two readings exceeds the tolerance (so the test cannot pass
+vacuously), then checks every product entry point against the oracle.  The
+one-hot case (x = e_k gives y = what[:, k] exactly, for every format) closes
+the set.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_group_wise_amd import q4
+from _helpers import DEV, TORCH_ACT, assert_product_ok, dev16, host16
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ]
+
+F16_ONE_PLUS = {1: 0x3C04, 3: 0x3C0C}  # fp16 1 + 2^-8 and 1 + 3 * 2^-8 (bf16 midpoints)
+
+
+def f16(v):
+    return np.asarray(v, np.float32).astype(np.float16).view(np.uint16)
+
+
+def tie_rows(fmt, g, N, K):
+    """fp16 weights whose dequantized values are mostly bf16 midpoints.
+
+    Group j of row r uses t = 1 + 2^-8 or 1 + 3 * 2^-8 (alternating) as the
+    level-1 value: NF4 blocks hold t everywhere (absmax t, code 15, what = t);
+    INT4-sym groups hold 7t (absmax, so the scale is exactly t) and +-t
+    (levels +-1); INT4-asym groups hold a maximum whose range / 15 rounds to
+    the fp16 scale t, then t (level 1, zero-point 0)."""
+    t_bits = [F16_ONE_PLUS[1], F16_ONE_PLUS[3]]
+    asym_hi = {F16_ONE_PLUS[1]: f16(15.0546875)[()], F16_ONE_PLUS[3]: f16(15.171875)[()]}
+    w = np.zeros((N, K), np.uint16)
+    for r in range(N):
+        for j in range(K // g):
+            t = t_bits[(r + j) % 2]
+            blk = np.full(g, t, np.uint16)
+            if fmt == q4.INT4_SYM:
+                tv = np.float32(np.uint16(t).view(np.float16))
+                blk[0] = f16(7 * tv)
+                blk[1::2] = t | 0x8000  # -t: level -1
+            elif fmt == q4.INT4_ASYM:
+                blk[0] = asym_hi[t]
+            w[r, j * g:(j + 1) * g] = blk
+    return w
+
+
+def unrounded(fmt, g, codes, scales, zeros, N, K):
+    """level * scale in float64 per weight (the scale-hoisted reading), from
+    the oracle's codes and scales; used only to choose x."""
+    nib = np.empty((N, K), np.int64)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    G = K // g
+    if fmt == q4.NF4:
+        s = scales.astype(np.float64).reshape(N, G)
+        lv = oracle.nf4_table().astype(np.float64)[nib]
+    elif fmt == q4.NF4_DQ:
+        qc, s2 = oracle.dq_split(scales, N * G)
+        c = (qc.astype(np.float32) * s2[np.arange(N * G) // oracle.DQ_BLOCK]).astype(np.float32)
+        s = c.astype(np.float64).reshape(N, G)
+        lv = oracle.nf4_table().astype(np.float64)[nib]
+    else:
+        s = scales.view(np.float16).astype(np.float64).reshape(N, G)
+        if fmt == q4.INT4_SYM:
+            lv = (nib - 8).astype(np.float64)
+        else:
+            zz = np.empty(2 * zeros.size, np.int64)
+            zz[0::2] = zeros & 0xF
+            zz[1::2] = zeros >> 4
+            lv = (nib - zz[: N * G].reshape(N, G).repeat(g, axis=1)).astype(np.float64)
+    return lv * s.repeat(g, axis=1)
+
+
+def adversarial_case(fmt, g, act, w, amp):
+    """Quantize w with the oracle and pick x = amp * sign(unrounded - what)
+    per weight (rows of x follow rows of w, cycling).  Returns the oracle
+    weight, x bits, and the per-row gap sum |x| * |unrounded - what|."""
+    N, K = w.shape
+    oc, os_, oz = oracle.quantize(fmt, g, w)
+    wd = oracle.dequantize(fmt, g, oc, os_, oz, N, K, act)
+    wd = (oracle.f16_bits_to_f32(wd) if act == q4.F16
+          else (wd.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    gap = unrounded(fmt, g, oc, os_, oz, N, K) - wd
+    xs = np.sign(gap) * amp
+    x = (f16(xs) if act == q4.F16
+         else (xs.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    return (oc, os_, oz), x, np.abs(gap).sum(1) * amp
+
+
+def _check_adversarial(oc_os_oz, x, gapsum, fmt, g, act, N, K, ratio):
+    oc, os_, oz = oc_os_oz
+    yr, ad = oracle.matmul(fmt, g, act, x[0:1], oc, os_, oz, N, K, rows=[0])
+    tol = oracle.tolerance(ad, yr, act)[0, 0]
+    assert gapsum[0] > ratio * tol, (
+        f"construction not adversarial: gap {gapsum[0]} vs tolerance {tol}")
+
+
+def _weight_on_gpu(fmt, g, w_bits, oc_os_oz):
+    q = q4.quantize(dev16(w_bits), fmt, g)
+    torch.cuda.synchronize()
+    oc, os_, oz = oc_os_oz
+    assert np.array_equal(q.codes.cpu().numpy(), oc)
+    return q
+
+
+def _products(fmt, g, act, q, x_bits, oc_os_oz, tag):
+    """Every product entry point on these x rows: q4_gemv at M = 1 and 2,
+    the chain (each row a task), the skinny product (M = 3 and 16), the
+    GEMM (M = 17), all against the oracle."""
+    oc, os_, oz = oc_os_oz
+    N, K = q.N, q.K
+    xt = dev16(x_bits, act)
+    Mx = x_bits.shape[0]
+    for M in (1, 2, 3, 16, 17):
+        rows = np.arange(M) % Mx
+        xm = xt[torch.from_numpy(rows).to(DEV)].contiguous()
+        y = q4.gemm(xm, q) if M > 16 else q4.gemv(xm, q)
+        torch.cuda.synchronize()
+        yr, ad = oracle.matmul(fmt, g, act, x_bits[rows], oc, os_, oz, N, K)
+        assert_product_ok(y, yr, ad, tag=f"{tag} M{M}")
+    if K <= q4.CHAIN_MAX_K:
+        tasks = [(xt[i:i + 1].contiguous(), q, None, q4.TASK_NO_WAIT) for i in range(min(Mx, 4))]
+        outs = q4.gemv_chain(tasks)
+        torch.cuda.synchronize()
+        for i, y in enumerate(outs):
+            yr, ad = oracle.matmul(fmt, g, act, x_bits[i:i + 1], oc, os_, oz, N, K)
+            assert_product_ok(y, yr, ad, tag=f"{tag} chain task {i}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_bf16_midpoint_weights(fmt, g):
+    """The verdict's construction, generalised: bf16 midpoints everywhere,
+    x = +-1 by rounding direction; K spans one and several chain stages."""
+    for N, K in [(24, 2048), (6, 8192 + 2 * g)]:
+        w = tie_rows(fmt, g, N, K)
+        case, x, gapsum = adversarial_case(fmt, g, q4.BF16, w, 1.0)
+        _check_adversarial(case, x, gapsum, fmt, g, q4.BF16, N, K, ratio=1.0)
+        q = _weight_on_gpu(fmt, g, w, case)
+        _products(fmt, g, q4.BF16, q, x, case, tag=f"bf16 ties fmt{fmt} g{g} {N}x{K}")
+
+
+def test_small_nf4_midpoint_row():
+    """The two-block row of the verdict: blocks of 1 + 2^-8 and 1 + 3 * 2^-8,
+    x = +1 then -1.  The reference is -1.0 (the bf16 weights are 1 and
+    1.015625); the scale-hoisted sum would give -0.5."""
+    w = np.concatenate([np.full(64, F16_ONE_PLUS[1], np.uint16),
+                        np.full(64, F16_ONE_PLUS[3], np.uint16)])[None, :]
+    x = np.concatenate([np.full(64, 0x3F80, np.uint16), np.full(64, 0xBF80, np.uint16)])[None, :]
+    oc, os_, oz = oracle.quantize(q4.NF4, 64, w)
+    yr, ad = oracle.matmul(q4.NF4, 64, q4.BF16, x, oc, os_, oz, 1, 128)
+    assert yr[0, 0] == -1.0
+    q = _weight_on_gpu(q4.NF4, 64, w, (oc, os_, oz))
+    xt = dev16(x, q4.BF16)
+    for y in (q4.gemv(xt, q), q4.gemv_chain([(xt, q, None)])[0]):
+        torch.cuda.synchronize()
+        assert float(y.float().cpu()[0, 0]) == -1.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_f16_subnormal_weights(fmt):
+    """Dequantized values in fp16's subnormal range (weights ~ 1e-6), x =
+    +-1000 by rounding direction.  For NF4 the gap exceeds the tolerance;
+    INT4 values there are exact multiples of the subnormal quantum or carry
+    at most 2^-11 relative rounding, and are checked the same way."""
+    g, N, K = 64, 16, 4096
+    rng = np.random.default_rng(55)
+    w = f16(rng.standard_normal((N, K)).astype(np.float32) * 1e-6)
+    case, x, gapsum = adversarial_case(fmt, g, q4.F16, w, 1000.0)
+    if fmt in (q4.NF4, q4.NF4_DQ):
+        _check_adversarial(case, x, gapsum, fmt, g, q4.F16, N, K, ratio=2.0)
+    q = _weight_on_gpu(fmt, g, w, case)
+    _products(fmt, g, q4.F16, q, x, case, tag=f"f16 subnormal fmt{fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("act", [q4.F16, q4.BF16])
+def test_one_hot_returns_dequantized_weight(fmt, act):
+    """x = e_k gives y[n] = what[n, k] exactly (one exact product, every other
+    term zero), through every product entry point; zeros compared as values
+    (the sign of a zero product is not specified)."""
+    g, N, K = 64, 72, 1024
+    rng = np.random.default_rng(7 + fmt)
+    w = f16(rng.standard_normal((N, K)).astype(np.float32) * 0.02)
+    w[3] = f16(rng.standard_normal(K).astype(np.float32) * 1e-6)   # tiny groups
+    w[5, :64] = 0                                                  # an all-zero group
+    q = q4.quantize(dev16(w), fmt, g)
+    deq = q4.dequantize(q, TORCH_ACT[act]).float()
+    ks = [0, 5, 63, 64, 511, K - 1]
+    one = 0x3C00 if act == q4.F16 else 0x3F80
+    x = np.zeros((len(ks), K), np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = one
+    xt = dev16(x, act)
+    want = deq[:, ks].t()
+    outs = {"gemv M1": torch.cat([q4.gemv(xt[i:i + 1], q) for i in range(len(ks))]),
+            "gemv M2": torch.cat([q4.gemv(xt[i:i + 2], q) for i in range(0, len(ks), 2)]),
+            "skinny": q4.gemv(xt, q),
+            "gemm": q4.gemm(torch.cat([xt, xt, xt, xt]), q)[: len(ks)],
+            "chain": torch.cat(q4.gemv_chain([(xt[i:i + 1], q, None, q4.TASK_NO_WAIT)
+                                              for i in range(len(ks))]))}
+    torch.cuda.synchronize()
+    for name, y in outs.items():
+        bad = (y.float() != want).nonzero()
+        assert bad.numel() == 0, f"{name} fmt{fmt} act{act}: {bad[:4].tolist()}"
