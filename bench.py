@@ -67,6 +67,9 @@ def parse():
                    help="decoder layers in the weight stream (32 for the 7B shape)")
     p.add_argument("--no-graph", action="store_true",
                    help="skip the graph-replayed single-launch comparison")
+    p.add_argument("--no-dep", action="store_true",
+                   help="skip the chain with a grid-wide wait before every product (its "
+                        "cooperative launch; for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="time budget of the CPU-oracle sample")
     p.add_argument("--skip-extra", action="store_true",
@@ -204,7 +207,7 @@ def main():
     token_single()
     torch.cuda.synchronize()
     ref = [y.clone() for y in flat_y]
-    for name, cs in (("independent", indep), ("dependent", dep)):
+    for name, cs in (("independent", indep),) + ((("dependent", dep),) if not args.no_dep else ()):
         for y in flat_y:
             y.zero_()
         run_chains(cs)
@@ -244,7 +247,7 @@ def main():
 
     timed = _timer(torch, stream)
     reps = max(args.steps // 5, 3)
-    dep_ms = timed(lambda: run_chains(dep), reps)
+    dep_ms = None if args.no_dep else timed(lambda: run_chains(dep), reps)
     single_ms = None
     if not args.no_graph:
         side = torch.cuda.Stream()
@@ -309,8 +312,9 @@ def main():
                       "(independent products)",
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
             "wall_ms_per_step": round(wall_ms / args.steps, 4),
-            "dependent_chain_ms_per_step": round(dep_ms, 4),
-            "dependent_chain_GBps": round(w_bytes / (dep_ms * 1e-3) / 1e9, 1),
+            "dependent_chain_ms_per_step": None if dep_ms is None else round(dep_ms, 4),
+            "dependent_chain_GBps": None if dep_ms is None
+            else round(w_bytes / (dep_ms * 1e-3) / 1e9, 1),
             "single_launch_graph_ms_per_step": None if single_ms is None else round(single_ms, 4),
             "single_launch_graph_GBps": None if single_ms is None
             else round(w_bytes / (single_ms * 1e-3) / 1e9, 1),

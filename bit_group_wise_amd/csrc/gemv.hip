@@ -56,10 +56,6 @@
 namespace q4 {
 namespace {
 
-// Steps (of 8 weights) between scheduling barriers in a stage; 0 = none.
-#ifndef Q4_GEMV_SB
-#define Q4_GEMV_SB 2
-#endif
 // Positions (stages) whose loads are kept in flight per wave, in the
 // single-product and the chained kernels.
 #ifndef Q4_GEMV_DEPTH
@@ -166,44 +162,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// Buffer views of one weight row n0: its codes, scales and zero-point bytes
-// (empty for n0 >= N, so a position past the last row loads zeros).  With
-// double-quantized absmax, `scales` covers the row's 8-bit absmax codes and
-// s2 points at the second-level constant of the run holding the row's first
-// group (the kernels receive the constants' base in place of `zeros`).
-struct RowViews {
-    __amdgpu_buffer_rsrc_t codes, scales, zeros;
+// One weight row: where its codes, scales and zero-points start (row `live`
+// false: past the last row, every load reads zero).  With double-quantized
+// absmax, `scales` points at the row's 8-bit absmax codes and s2 at the
+// second-level constant of the run holding the row's first group (the
+// kernels receive the constants' base in place of `zeros`).
+struct RowRef {
+    const uint8_t *codes;
+    const char *scales;
+    const uint8_t *zeros;  // asym: the byte holding the row's first zero-point nibble
+    const float *s2;
     int zpar;  // parity of the row's first flat group index (asym), or its
                // position in its run of kDqRun groups (double quantization)
-    const float *s2;
+    bool live;
 };
 
 template <int FMT>
-__device__ __forceinline__ RowViews row_views(const uint8_t *codes, const void *scales,
-                                              const uint8_t *zeros, int64_t n0, int64_t N,
-                                              int64_t row_bytes, int64_t G)
+__device__ __forceinline__ RowRef row_ref(const uint8_t *codes, const void *scales,
+                                          const uint8_t *zeros, int64_t n0, int64_t N,
+                                          int64_t row_bytes, int64_t G)
 {
     constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
-    const bool live = n0 < N;
-    RowViews v;
-    v.s2 = nullptr;
-    v.codes = make_rsrc(codes + n0 * row_bytes, live ? row_bytes : 0);
-    v.scales = make_rsrc((const char *)scales + n0 * G * ss, live ? G * ss : 0);
-    const int64_t g0 = n0 * G;
-    v.zpar = (int)(g0 & 1);
-    if constexpr (FMT == Q4_INT4_ASYM) {
-        v.zeros = make_rsrc(zeros + (g0 >> 1), live ? ((g0 + G - 1) >> 1) - (g0 >> 1) + 1 : 0);
-    } else if constexpr (FMT == Q4_NF4_DQ) {
-        // g0 >= 0: shifts instead of signed division; a row past the end
-        // points at the first constant (read, never used: its codes are 0)
-        const uint64_t ug0 = (uint64_t)g0;
-        v.s2 = (const float *)zeros + (live ? ug0 >> 8 : 0);
-        v.zpar = (int)(ug0 & (kDqRun - 1));
-        v.zeros = v.codes;
-    } else {
-        v.zeros = v.codes;
+    RowRef r;
+    r.live = n0 < N;
+    r.codes = codes + n0 * row_bytes;
+    r.scales = (const char *)scales + n0 * G * ss;
+    const uint64_t g0 = (uint64_t)(n0 * G);
+    r.zeros = zeros + (g0 >> 1);
+    r.zpar = (int)(g0 & 1);
+    r.s2 = nullptr;
+    if constexpr (FMT == Q4_NF4_DQ) {
+        // a row past the end points at the first constant (read, never
+        // used: its codes are 0)
+        r.s2 = (const float *)zeros + (r.live ? g0 >> 8 : 0);
+        r.zpar = (int)(g0 & (kDqRun - 1));
     }
-    return v;
+    return r;
 }
 
 // One pipeline stage of a wave: 128 chunks of 32 weights of one row; lane l
@@ -224,53 +218,85 @@ struct Stage {
 // Chunk of half h of stage s for a lane.
 __device__ __forceinline__ int stage_chunk(int s, int lane, int h) { return kStageChunks * s + 64 * h + lane; }
 
+// A lane's offsets into the per-stage views (constant for the kernel): its
+// chunk's codes and scale, and (asym) the byte and nibble of its group's
+// zero-point for either parity of the row's first flat group.
+struct LaneOffs {
+    uint32_t cd[2], sc[2], zb[2][2], zsh[2][2];
+};
+template <int FMT>
+__device__ __forceinline__ LaneOffs lane_offs(int lane, int gshift)
+{
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    LaneOffs o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lc = 64 * h + lane;      // chunk within the stage
+        const int gl = (32 * lc) >> gshift;  // its group within the stage
+        o.cd[h] = 16 * lc;
+        o.sc[h] = ss * gl;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            o.zb[p][h] = (p + gl) >> 1;
+            o.zsh[p][h] = 4 * ((p + gl) & 1);
+        }
+    }
+    return o;
+}
+
 // Non-temporal loads: the weights are streamed once per product, so they are
 // not kept in the caches (the "nt" cache-policy bit).
 constexpr int kNT = 2;
 
-// Chunks past the row end (C chunks per row) are sent out of the row's
-// views, so they read zeros without touching memory (their activations are
-// zero as well).
+// The loads of stage s of a row.  Each array is read through a view that
+// starts at the stage's first byte and ends at the row's last (built with
+// scalar arithmetic), and every lane uses its constant offset: the buffer
+// unit's range check then returns zeros for chunks past the row end and for
+// a row past the last one (an empty view), without any per-lane arithmetic
+// and without touching memory outside the row.
 template <int FMT>
-__device__ __forceinline__ void load_stage(Stage &st, const RowViews &v, int s, int lane, int gshift,
-                                           int C)
+__device__ __forceinline__ void load_stage(Stage &st, const RowRef &r, int s, const LaneOffs &lo,
+                                           int row_bytes, int G, int gshift)
 {
+    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    const int cs = 16 * kStageChunks * s;                 // the stage's first code byte
+    const int gs = (kStageChunks * 32 * s) >> gshift;      // the stage's first group in the row
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(r.codes + cs, r.live ? row_bytes - cs : 0);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(r.scales + gs * ss, r.live ? (G - gs) * ss : 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int ch = stage_chunk(s, lane, h);
-        const bool in = ch < C;
-        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, in ? 16 * ch : -16, 0, kNT);
-        const int gl = (32 * ch) >> gshift;  // group index within the row
+        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(cr, lo.cd[h], 0, kNT);
         if constexpr (FMT == Q4_NF4)
-            st.sc[h] = std::bit_cast<float>(
-                __builtin_amdgcn_raw_buffer_load_b32(v.scales, in ? 4 * gl : -16, 0, kNT));
+            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(sr, lo.sc[h], 0, kNT));
         else if constexpr (FMT == Q4_NF4_DQ)  // the 8-bit code; the constant below
-            st.sc[h] = std::bit_cast<float>((uint32_t)
-                __builtin_amdgcn_raw_buffer_load_b8(v.scales, in ? gl : -16, 0, kNT));
+            st.sc[h] = std::bit_cast<float>((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, lo.sc[h], 0, kNT));
         else
-            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(v.scales, in ? 2 * gl : -16, 0, kNT));
-        if constexpr (FMT == Q4_INT4_ASYM) {
-            const int gz = gl + v.zpar;
-            const uint32_t b =
-                __builtin_amdgcn_raw_buffer_load_b8(v.zeros, in ? gz >> 1 : -16, 0, kNT);
-            st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
-        } else {
-            st.zf[h] = 0.0f;
+            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(sr, lo.sc[h], 0, kNT));
+        st.zf[h] = 0.0f;
+    }
+    if constexpr (FMT == Q4_INT4_ASYM) {
+        // nibble zpar + gs + gl of the row's zero-point bytes; gs is even
+        const __amdgpu_buffer_rsrc_t zr =
+            make_rsrc(r.zeros + (gs >> 1), r.live ? (G - gs + r.zpar + 1) >> 1 : 0);
+        const int p = r.zpar;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(zr, p ? lo.zb[1][h] : lo.zb[0][h], 0, kNT);
+            st.zf[h] = (float)((b >> (p ? lo.zsh[1][h] : lo.zsh[0][h])) & 0xf);
         }
     }
     if constexpr (FMT == Q4_NF4_DQ) {
         // One scalar load of the constants of the row's runs (a row of at
         // most 16384 / 32 groups touches at most 3 runs; the last ones may
-        // read the buffer's padding, never used), rather than a vector load
-        // per stage: the vector memory instructions per stage are what the
-        // loop's rate is most sensitive to.  The group's run is picked when
-        // the stage is computed.
+        // read the buffer's padding, never used for a real group), rather
+        // than a vector load per stage.  The group's run is picked when the
+        // stage is computed.
         typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
-        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)v.s2;
+        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)r.s2;
         st.s2[0] = c[0];
         st.s2[1] = c[1];
         st.s2[2] = c[2];
-        st.zpar = v.zpar;
+        st.zpar = r.zpar;
     }
 }
 
@@ -303,22 +329,37 @@ __device__ __forceinline__ void load_x(u32x4 (&xv)[MT], const uint32_t *xs,
 // Sum of the diagonal of a lane-own-dot 16 x 16 accumulator: entry (n, n)
 // is register n % 4 of lane n + 16 (n / 4), i.e. of the lanes whose
 // position in their 16-lane row is in quad (lane / 16).  Every lane gets
-// the total.
+// the total.  (Selects by per-lane conditions, so no branch: the other
+// entries may hold anything, Inf included, and never reach the sum.)
 __device__ __forceinline__ float diag_sum(const f32x4 &a, int lane)
 {
-    const int r = lane & 3;
-    float d = r == 0 ? a[0] : (r == 1 ? a[1] : (r == 2 ? a[2] : a[3]));
+    const float a01 = (lane & 1) ? a[1] : a[0];
+    const float a23 = (lane & 1) ? a[3] : a[2];
+    float d = (lane & 2) ? a23 : a01;
     d = ((lane & 15) >> 2) == (lane >> 4) ? d : 0.0f;
     return wave_sum(d);
+}
+
+// Table lookups of one code dword: the binary32 level pairs of its 4 bytes.
+__device__ __forceinline__ void lookup4(uint32_t w, uint32_t laneoff, const uint32_t *__restrict__ tbl,
+                                        float2 (&lv)[4])
+{
+    constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, laneoff, kSel[k]);
+        lv[k] = *(const float2 *)((const char *)tbl + addr);
+    }
 }
 
 // Products of one stage: 8 steps of 8 weights (two chunks x four dwords of
 // codes).  Per code byte: its LDS address by one v_perm, one 8-byte table
 // read (the two nibbles' binary32 levels), two fma with the chunk's scale
 // and bias and one packed conversion to the activation dtype; per dword one
-// matrix-core product per activation row.  Scheduling barriers every
-// Q4_GEMV_SB steps keep the table reads of later steps from being hoisted
-// (which would exhaust the register budget).
+// matrix-core product per activation row.  The lookups of the next dword
+// are issued before the current one is converted (scheduling barriers keep
+// that order), so a table read's latency hides behind a dword of
+// arithmetic.
 template <int FMT, int ACT, int MT, int XS>
 __device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
                                               const uint32_t *__restrict__ tbl, const uint32_t *xs,
@@ -326,19 +367,12 @@ __device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
                                               __amdgpu_buffer_rsrc_t xr, int K, int xrow, int s,
                                               int lane, int C, uint32_t laneoff, int gshift)
 {
-    constexpr uint32_t kSel[4] = {0x0c0c0400u, 0x0c0c0500u, 0x0c0c0600u, 0x0c0c0700u};
     constexpr bool nf4 = level_fmt(FMT) == Q4_NF4;
-    u32x4 xv[MT];
-    if constexpr (XS == X_REG) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            xv[m] = xreg[m * 8];
-    } else {
-        load_x<MT, XS>(xv, xs, xr, K, xrow, stage_chunk(s, lane, 0), C, 0);
-    }
+    // scale and bias of each half
+    float sc[2], bias[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float sc = st.sc[h];
+        sc[h] = st.sc[h];
         if constexpr (FMT == Q4_NF4_DQ) {
             // The half's 64 chunks cover at most 64 groups, so at most
             // two runs: the run of its first group (ra) and the next
@@ -361,50 +395,58 @@ __device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
             // bits): c' = 0 there without the product.  For a real group
             // with qc = 0 this is the same +0 as the product.
             const uint32_t qc = std::bit_cast<uint32_t>(st.sc[h]);
-            sc = qc != 0 ? keep_f32((float)qc * s2) : 0.0f;
+            sc[h] = qc != 0 ? keep_f32((float)qc * s2) : 0.0f;
         }
-        const float bias = chunk_bias<FMT>(sc, st.zf[h]);
+        bias[h] = chunk_bias<FMT>(sc[h], st.zf[h]);
+    }
+    u32x4 xv[MT];
+    if constexpr (XS == X_REG) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x4 xn[MT];
-            if (h * 4 + j < 7) {
-                if constexpr (XS == X_REG) {
+        for (int m = 0; m < MT; ++m)
+            xv[m] = xreg[m * 8];
+    } else {
+        load_x<MT, XS>(xv, xs, xr, K, xrow, stage_chunk(s, lane, 0), C, 0);
+    }
+    float2 lv[2][4];
+    lookup4(st.cw[0][0], laneoff, tbl, lv[0]);
 #pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        xn[m] = xreg[m * 8 + h * 4 + j + 1];
-                } else {
-                    load_x<MT, XS>(xn, xs, xr, K, xrow, stage_chunk(s, lane, j == 3 ? h + 1 : h),
-                                   C, (j + 1) & 3);
-                }
-            }
-            u32x4 wf;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t addr = __builtin_amdgcn_perm(st.cw[h][j], laneoff, kSel[k]);
-                const float2 lv = *(const float2 *)((const char *)tbl + addr);
-                float w0 = __builtin_fmaf(lv.x, sc, bias);
-                float w1 = __builtin_fmaf(lv.y, sc, bias);
-                if constexpr (nf4) {
-                    // rounded to binary32 first, then to the activation
-                    // dtype (no single-rounding mixed fma)
-                    w0 = keep_f32(w0);
-                    w1 = keep_f32(w1);
-                }
-                wf[k] = ACT == Q4_BF16 ? pack_bf2(w0, w1) : pack_h2(w0, w1);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                acc[m] = mfma<ACT>(wf, xv[m], acc[m]);
-            if (h * 4 + j < 7) {
+    for (int t = 0; t < 8; ++t) {  // step t: dword t & 3 of half t >> 2
+        const int h = t >> 2;
+        u32x4 xn[MT];
+        if (t < 7) {
+            lookup4(st.cw[(t + 1) >> 2][(t + 1) & 3], laneoff, tbl, lv[(t + 1) & 1]);
+            if constexpr (XS == X_REG) {
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    xv[m] = xn[m];
+                    xn[m] = xreg[m * 8 + t + 1];
+            } else {
+                load_x<MT, XS>(xn, xs, xr, K, xrow, stage_chunk(s, lane, (t + 1) >> 2), C,
+                               (t + 1) & 3);
             }
-#if Q4_GEMV_SB > 0
-            if ((j + 1) % Q4_GEMV_SB == 0)
-                __builtin_amdgcn_sched_barrier(0);
-#endif
         }
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 wf;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float w0 = __builtin_fmaf(lv[t & 1][k].x, sc[h], bias[h]);
+            float w1 = __builtin_fmaf(lv[t & 1][k].y, sc[h], bias[h]);
+            if constexpr (nf4) {
+                // rounded to binary32 first, then to the activation dtype
+                // (no single-rounding mixed fma)
+                w0 = keep_f32(w0);
+                w1 = keep_f32(w1);
+            }
+            wf[k] = ACT == Q4_BF16 ? pack_bf2(w0, w1) : pack_h2(w0, w1);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[m] = mfma<ACT>(wf, xv[m], acc[m]);
+        if (t < 7) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                xv[m] = xn[m];
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -493,6 +535,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 
     // ring of P in-flight positions (a row past the end has an empty view,
     // so its loads return zeros and it is never computed)
+    const LaneOffs lo = lane_offs<FMT>(lane, gshift);
     Pos pos[P];
     Stage st[P];
     pos[0] = Pos{(int)__builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6)), 0};
@@ -500,8 +543,8 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
     for (int q = 0; q < P; ++q) {
         if (q > 0)
             pos[q] = advance(pos[q - 1]);
-        const RowViews v = row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-        load_stage<FMT>(st[q], v, pos[q].s, lane, gshift, C);
+        load_stage<FMT>(st[q], row_ref<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G),
+                        pos[q].s, lo, row_bytes, G, gshift);
     }
 
     fill_level_table<FMT, kBlock>(tbl);
@@ -548,9 +591,8 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
             // refill this slot with the position P steps ahead
             pos[q] = advance(pos[(q + P - 1) % P]);
             {
-                const RowViews v =
-                    row_views<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G);
-                load_stage<FMT>(st[q], v, pos[q].s, lane, gshift, C);
+                load_stage<FMT>(st[q], row_ref<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G),
+                                pos[q].s, lo, row_bytes, G, gshift);
             }
             if (cp.s == S - 1) {
                 float out = 0.0f;
@@ -617,104 +659,44 @@ struct ChainArgs {
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a second)
 constexpr int kChainMaxK = 16384;  // 4 stages: a task and the next fit the 8 slots
 
-// A wave's position in the chain: task, row and stage along K; whether the
-// stage is the row's last, where the row's output goes and the task's first
-// x slot.
-struct CPos {
-    int t, row, s;
-    bool last;
-    uint16_t *yp;
-    int xbase;
-};
-
 __host__ __device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
 
-// The views of one task for the chained kernel: whole arrays (each under
-// 2 GiB, checked on the host), with a row's and a stage's place added as a
-// wave-uniform offset, so that moving to the next row costs a few scalar
-// instructions and no reload of the task's arguments.  Lanes whose chunk is
-// past the row end are sent past the view by kChainOob.
+// One task's arrays and sizes, kept in scalar registers while a wave works
+// on the task: a row's and a stage's views are built from them with a few
+// scalar instructions, without reloading the task's arguments.
 struct TaskViews {
-    __amdgpu_buffer_rsrc_t codes, scales, zeros;
-    const float *s2;  // double quantization: the second-level constants
+    const uint8_t *codes;
+    const void *scales;
+    const uint8_t *zeros;  // asym: zero-points; double quantization: the constants
     uint16_t *y;
     int N, S, C, row_bytes, G, xbase;
 };
-constexpr uint32_t kChainOob = 0x80000000u;
 
 template <int FMT>
 __device__ __forceinline__ TaskViews task_views(const ChainTask &T, int gshift)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     TaskViews v;
     v.N = T.N;
     v.row_bytes = T.K >> 1;
     v.G = T.K >> gshift;
     v.C = T.K >> 5;
     v.S = chain_stages(T.K);
-    v.codes = make_rsrc(T.codes, (int64_t)v.N * v.row_bytes);
-    v.scales = make_rsrc(T.scales, (int64_t)v.N * v.G * ss);
-    v.zeros = FMT == Q4_INT4_ASYM ? make_rsrc(T.zeros, ((int64_t)v.N * v.G + 1) / 2) : v.codes;
-    v.s2 = (const float *)T.zeros;
+    v.codes = T.codes;
+    v.scales = T.scales;
+    v.zeros = T.zeros;
     v.y = T.y;
     v.xbase = ctl_base(T.ctl);
     return v;
 }
 
-// The loads of stage s of row `row` (row == N: past the last row, every load
-// is out of the views and returns zero), as load_stage does with row views.
-// The row's and the stage's place is added to the lane's offset (voffset),
-// which the buffer unit range-checks against the view (a load's soffset is
-// not checked), so a position past the last row or a chunk past the row
-// end reads zeros and never touches memory outside the task's arrays.
+// The loads of stage s of row `row` of a task (row == N: past the last row,
+// every load returns zero).
 template <int FMT>
 __device__ __forceinline__ void load_stage_chain(Stage &st, const TaskViews &tv, int row, int s,
-                                                 int lane, int gshift)
+                                                 const LaneOffs &lo, int gshift)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
-    const int g0 = row * tv.G;                                // the row's first flat group
-    const int gs = (kStageChunks * 32 * s) >> gshift;          // the stage's first group in the row
-    const uint32_t cd_off = (uint32_t)(row * tv.row_bytes + 16 * kStageChunks * s);
-    const uint32_t sc_off = (uint32_t)((g0 + gs) * ss);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int lc = 64 * h + lane;                         // chunk within the stage
-        const bool in = kStageChunks * s + lc < tv.C;
-        st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(tv.codes, in ? cd_off + 16 * lc : kChainOob,
-                                                         0, kNT);
-        const int gl = (32 * lc) >> gshift;                    // group within the stage
-        if constexpr (FMT == Q4_NF4)
-            st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(
-                tv.scales, in ? sc_off + 4 * gl : kChainOob, 0, kNT));
-        else if constexpr (FMT == Q4_NF4_DQ)
-            st.sc[h] = std::bit_cast<float>((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-                tv.scales, in ? sc_off + gl : kChainOob, 0, kNT));
-        else
-            st.sc[h] = h2f(__builtin_amdgcn_raw_buffer_load_b16(
-                tv.scales, in ? sc_off + 2 * gl : kChainOob, 0, kNT));
-        if constexpr (FMT == Q4_INT4_ASYM) {
-            // nibble g0 + gs + gl; gs is even, so the byte is
-            // (g0 >> 1) + gs / 2 + ((g0 & 1) + gl) / 2
-            const int gz = (g0 & 1) + gl;
-            const uint32_t z_off = (uint32_t)((g0 >> 1) + (gs >> 1));
-            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
-                tv.zeros, in ? z_off + (gz >> 1) : kChainOob, 0, kNT);
-            st.zf[h] = (float)((b >> ((gz & 1) * 4)) & 0xf);
-        } else {
-            st.zf[h] = 0.0f;
-        }
-    }
-    if constexpr (FMT == Q4_NF4_DQ) {
-        // the constants of the row's runs, as load_stage reads them (a row
-        // past the end reads the first ones, never used)
-        typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
-        const float *p = tv.s2 + (row < tv.N ? (g0 >> 8) : 0);
-        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)p;
-        st.s2[0] = c[0];
-        st.s2[1] = c[1];
-        st.s2[2] = c[2];
-        st.zpar = g0 & (kDqRun - 1);
-    }
+    load_stage<FMT>(st, row_ref<FMT>(tv.codes, tv.scales, tv.zeros, row, tv.N, tv.row_bytes, tv.G),
+                    s, lo, tv.row_bytes, tv.G, gshift);
 }
 
 // s_waitcnt on vector memory only (expcnt and lgkmcnt left at their maxima).
@@ -992,90 +974,18 @@ void gemv_chain_kernel(const ChainArgs a)
         }
     } else {
         // ---------------------------------------------------------- compute
-        // vector-memory instructions per ring refill
+        // A wave's walk, task by task: in each task it takes rows first,
+        // first + step, ... below end (a segment).  With no waiting task the
+        // rows are those of the workgroup's block, dealt to its waves in
+        // turn (continuing the turn across tasks); otherwise task t's rows
+        // are dealt to all the grid's waves from a rotated start, so that
+        // the waves holding one row more than the others differ from task
+        // to task.  Inside a segment the ring is the single-product
+        // kernel's: a position is a row and a stage, advanced with a few
+        // scalar instructions; task switches stay out of that loop.
         const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * kChainCompute + wave);
+        const LaneOffs lo = lane_offs<FMT>(lane, a.gshift);
         const int total_waves = gridDim.x * kChainCompute;
-        // A wave's walk: its rows in order and each row's stages.  With no
-        // waiting task, the rows are those of the workgroup's block, dealt
-        // to its waves in turn.  Otherwise the walk goes task by task: task
-        // t's rows are dealt to all the grid's waves from a rotated start,
-        // so that the waves holding one row more than the others differ
-        // from task to task.
-        // tv: the views of the newest position's task (positions are made
-        // and loaded in order, so the newest is always the one loaded)
-        TaskViews tv = task_views<FMT>(task(tlo < nt ? tlo : 0), a.gshift);
-        // a position past this wave's rows: a row past the end of the
-        // current views
-        auto past = [&]() { return CPos{nt, tv.N, 0, false, tv.y, 0}; };
-        // blocked walk: wave w takes rows w, w + 15, ... of the block
-        auto in_block = [&](int u, int r) { return u < tend || (u == tend && r < rend); };
-        auto block_pos = [&](int u, int r) {
-            // row r of task u, or the first row after it when r >= N_u
-            while (u < nt) {
-                const int n = task(u).N;
-                if (r < n)
-                    break;
-                r -= n;
-                ++u;
-            }
-            if (!in_block(u, r))
-                return past();
-            tv = task_views<FMT>(task(u), a.gshift);
-            return CPos{u, r, 0, tv.S == 1, tv.y + r, tv.xbase};
-        };
-        auto first_pos = [&](int t) {
-            if constexpr (!DEP)
-                return has_rows ? block_pos(tlo, rlo + wave) : past();
-            for (; t < nt; ++t) {
-                const int e =
-                    (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
-                const ChainTask T = task(t);
-                if (e < T.N) {
-                    tv = task_views<FMT>(T, a.gshift);
-                    return CPos{t, e, 0, tv.S == 1, tv.y + e, tv.xbase};
-                }
-            }
-            // past the last task: a row past the end of the last views
-            return past();
-        };
-        auto advance = [&](CPos q) {
-            if (q.t >= nt)
-                return q;
-            if (++q.s == tv.S) {
-                q.s = 0;
-                if constexpr (!DEP) {
-                    const int r = q.row + kChainCompute;
-                    if (r >= tv.N || !in_block(q.t, r))
-                        return block_pos(q.t, r);
-                    q.row = r;
-                    q.yp += kChainCompute;
-                } else {
-                    q.row += total_waves;
-                    q.yp += total_waves;
-                    if (q.row >= tv.N)
-                        return first_pos(q.t + 1);
-                }
-            }
-            q.last = q.s == tv.S - 1;
-            return q;
-        };
-        // Refills are issued unconditionally (past the last task with every
-        // load out of the views: they return zeros) so that the number of
-        // loads in flight is the same on every path and the waits stay
-        // partial.
-        auto load_pos = [&](Stage &st, CPos q) {
-            load_stage_chain<FMT>(st, tv, q.row, q.s, lane, a.gshift);
-        };
-        CPos pos[P];
-        Stage st[P];
-        pos[0] = first_pos(0);
-#pragma unroll
-        for (int q = 0; q < P; ++q) {
-            if (q > 0)
-                pos[q] = advance(pos[q - 1]);
-            st[q] = Stage{};
-            load_pos(st[q], pos[q]);
-        }
         __syncthreads();  // the table, the counters and x of task tlo
         int cur = tlo;
         // Entering task cur + 1: count in, then wait for its x.  Before a
@@ -1098,49 +1008,79 @@ void gemv_chain_kernel(const ChainArgs a)
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
         };
 
-        // The ring: position q is computed while the next ones arrive, then
-        // its slot is refilled with the position P ahead.  A position of a
-        // later task first enters that task (and any task between without
-        // rows for this wave).  Each lane keeps its x slice (chunks l and
-        // 64 + l of the position's stage) in registers, read from LDS when
-        // the task or the stage changes.
-        //
-        // A round of the ring is never left in the middle (the load waits
-        // stay partial only if every path refills every slot): a position
-        // past the last task has loaded zeros from an empty view; it is
-        // computed on them and writes nothing.
         u32x4 xreg[8];
-        int xkey = -1;
         f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-        while (pos[0].t < nt) {
+        int turn = 0;  // blocked walk: the block's rows before this task, mod 15
+        const int t0 = has_rows ? tlo : nt;
+        for (int t = t0; t <= thi; ++t) {
+            const ChainTask T = task(t);
+            const TaskViews tv = task_views<FMT>(T, a.gshift);
+            int first, step, end;
+            if constexpr (!DEP) {
+                const int start = t == tlo ? rlo : 0;
+                end = (t == tend) ? rend : tv.N;
+                first = start + (wave - turn + kChainCompute) % kChainCompute;
+                step = kChainCompute;
+                turn = (turn + end - start) % kChainCompute;
+            } else {
+                first = (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
+                step = total_waves;
+                end = tv.N;
+            }
+            if (first >= end)
+                continue;  // no rows here (the task is still entered below or at the end)
+            const int S = tv.S;
+            // positions: rows first, first + step, ...; a row at or past end
+            // loads from an empty view (zeros) and stores nothing
+            auto advance = [&](Pos q) {
+                if (++q.s == S) {
+                    q.s = 0;
+                    q.row += step;
+                }
+                return q;
+            };
+            auto load_pos = [&](Stage &st_, Pos q) {
+                load_stage_chain<FMT>(st_, tv, q.row < end ? q.row : tv.N, q.s, lo, a.gshift);
+            };
+            // the first loads go out before the task's x is awaited (weights
+            // never depend on earlier tasks)
+            Pos pos[P];
+            Stage st[P];
+            pos[0] = Pos{first, 0};
 #pragma unroll
             for (int q = 0; q < P; ++q) {
-                const CPos cp = pos[q];
-                const bool live = cp.t < nt;
-                if (live) {
-                    while (cur < cp.t)
-                        enter();
-                }
-                const int key = 8 * cp.t + cp.s;
-                if (key != xkey) {
-                    chain_x_slice(xreg, xb, cp.xbase, cp.s, lane);
-                    xkey = key;
-                }
-                // (x comes from registers: no x view, K or chunk count needed)
-                compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
-                                                  make_rsrc(nullptr, 0), 0, 0, cp.s, lane, 0,
-                                                  laneoff, a.gshift);
-                if (cp.last) {
-                    const float out = diag_sum(acc[0], lane);
-                    acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (live && lane == 0)
-                        // through a global (not flat) pointer: a flat store may
-                        // write LDS, so LDS reads after it would wait for it
-                        *(__attribute__((address_space(1))) uint16_t *)cp.yp =
-                            (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
-                }
-                pos[q] = advance(pos[(q + P - 1) % P]);
+                if (q > 0)
+                    pos[q] = advance(pos[q - 1]);
                 load_pos(st[q], pos[q]);
+            }
+            while (cur < t)
+                enter();
+            if (S == 1)
+                chain_x_slice(xreg, xb, tv.xbase, 0, lane);
+            // A round of the ring is never left in the middle (the load
+            // waits stay partial only if every path refills every slot).
+            while (pos[0].row < end) {
+#pragma unroll
+                for (int q = 0; q < P; ++q) {
+                    const Pos cp = pos[q];
+                    if (S > 1)
+                        chain_x_slice(xreg, xb, tv.xbase, cp.s, lane);
+                    // (x comes from registers: no x view, K or chunk count needed)
+                    compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
+                                                      make_rsrc(nullptr, 0), 0, 0, cp.s, lane, 0,
+                                                      laneoff, a.gshift);
+                    if (cp.s == S - 1) {
+                        const float out = diag_sum(acc[0], lane);
+                        acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        if (cp.row < end && lane == 0)
+                            // through a global (not flat) pointer: a flat store
+                            // may write LDS, so LDS reads after it would wait
+                            *(__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row) =
+                                (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                    }
+                    pos[q] = advance(pos[(q + P - 1) % P]);
+                    load_pos(st[q], pos[q]);
+                }
             }
         }
         // waves with no rows in the last tasks still count into them
