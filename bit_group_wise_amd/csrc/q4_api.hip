@@ -5,11 +5,46 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "q4.h"
 #include "q4_internal.hpp"
 
+// The sync words of q4_gemv_chain_static: one chain's grid-barrier
+// arrivals, finished workgroups and timeout flag (Q4_GEMV_CHAIN_SYNC_BYTES),
+// in static device memory that each GPU holds for the life of the process.
+// In host code this name is not a device address; the address of each
+// device's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint32_t scratch[Q4_GEMV_CHAIN_SYNC_BYTES / 4];
+
 namespace {
+
+// Device address of `scratch` on each device, looked up once per device
+// with that device current (every GPU holds its own copy at its own
+// address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_for_current_device(uint32_t **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = (uint32_t *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool format_ok(q4_format f)
 {
@@ -219,6 +254,21 @@ q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *
         return st;
     if (!aligned(sync, 16))
         return Q4_EALIGN;
+    return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
+}
+
+q4_status q4_gemv_chain_static(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                               int ntasks, void *stream)
+{
+    q4_status st = check_chain(f, g, act_t, tasks, ntasks);
+    if (st != Q4_OK)
+        return st;
+    uint32_t *sync = nullptr;
+    if (scratch_for_current_device(&sync) != hipSuccess)
+        return Q4_EHIP;
+    // The kernel leaves the arrival and finish counters (words 0 and 1) at
+    // zero when it ends, as static device memory starts; the timeout flag
+    // (word 2) is sticky and not reported here.
     return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
 }
 

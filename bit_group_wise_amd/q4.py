@@ -33,6 +33,7 @@ SIGNATURES = {
     "q4_gemm": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "q4_gemm_dx": (_int, [_int, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "q4_gemv_chain": (_int, [_int, _int, _int, ctypes.c_void_p, _int, _vp, _vp]),
+    "q4_gemv_chain_static": (_int, [_int, _int, _int, ctypes.c_void_p, _int, _vp]),
     "q4_status_str": (ctypes.c_char_p, [_int]),
 }
 
@@ -293,4 +294,14 @@ def gemv_chain(tasks, sync=None):
     st = lib().q4_gemv_chain(fmt, g, act, ctypes.addressof(arr), len(tasks), _ptr(sync),
                              _stream_ptr(tasks[0][0]))
     _check(st, "q4_gemv_chain")
+    return outs
+
+
+def gemv_chain_static(tasks):
+    """q4_gemv_chain_static: the same chain with the library's static sync
+    words (no sync buffer; the outputs are allocated here unless given)."""
+    arr, outs, fmt, g, act = _chain_tasks(tasks)
+    st = lib().q4_gemv_chain_static(fmt, g, act, ctypes.addressof(arr), len(tasks),
+                                    _stream_ptr(tasks[0][0]))
+    _check(st, "q4_gemv_chain_static")
     return outs

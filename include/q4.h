@@ -219,6 +219,23 @@ typedef struct {
 q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
                         int ntasks, uint32_t *sync, void *stream);
 
+/* q4_gemv_chain without the sync buffer, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * allocation): the sync words live in a static device array of
+ * Q4_GEMV_CHAIN_SYNC_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  Same tasks, limits, status codes and results as
+ * q4_gemv_chain (the chain's size limits bound everything the array holds,
+ * so no larger input needs more of it).  It calls no allocating routine:
+ * the array's device address is looked up once per device, on the first
+ * call with that device current, and a failed lookup returns Q4_EHIP.  The
+ * kernel leaves the barrier counters at zero for the next call; the timeout
+ * flag (word 2 of the sync words) is not reported.  All calls on one GPU
+ * share the array: chains that may overlap on one GPU (different streams,
+ * or one call still running while another is enqueued elsewhere) race and
+ * must use q4_gemv_chain with their own sync buffers instead. */
+q4_status q4_gemv_chain_static(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *tasks,
+                               int ntasks, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *q4_status_str(q4_status s);
 
