@@ -652,11 +652,66 @@ struct ChainArgs {
     ChainTask t[kChainMax];
     int ntasks;
     int gshift;
-    // [0] barrier arrivals and [1] finished workgroups (zero on entry, left
-    // zero on exit); [2] set to 1 when a barrier wait ran out
+    // the sync words (layout below: zero on entry, left zero on exit except
+    // the timeout flag, set to 1 when a wait ran out)
     uint32_t *sync;
 };
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a second)
+
+// Layout of the sync buffer, in 32-bit words (one 128-byte line holds 32):
+// line 0 the finished-workgroup count and the timeout flag, then the grid
+// barrier's words each on a line of its own so that the atomics and polls
+// of different groups do not contend -- kBarGroups arrival counters, the
+// top-level counter, kBarGroups release flags.
+constexpr int kSyncLine = 32;
+constexpr int kBarGroups = 8;
+constexpr int kSyncDone = 0;
+constexpr int kSyncTimeout = 2;
+constexpr int kSyncArrive = kSyncLine;                       // + kSyncLine * group
+constexpr int kSyncTop = kSyncLine * (1 + kBarGroups);
+constexpr int kSyncFlag = kSyncLine * (2 + kBarGroups);      // + kSyncLine * group
+static_assert(4 * (kSyncFlag + kSyncLine * kBarGroups) <= Q4_GEMV_CHAIN_SYNC_BYTES,
+              "sync buffer too small");
+
+// Grid barrier number `nbar` of a chain (one thread per workgroup).  Two
+// levels, so that no counter takes more than a few dozen atomics per
+// barrier: workgroup b arrives at group b % 8's counter; the last arrival
+// of a group arrives at the top counter; the last group's last arrival
+// raises every group's release flag to nbar, and each workgroup polls its
+// own group's flag.  The counters only grow during a chain (barrier n is
+// complete at n times the arrivals), so no barrier resets them.  Each
+// arrival releases its workgroup's outputs; a group's last arrival
+// acquires the others' before it passes them on (release sequence on the
+// counter, then an acquire fence), and the caller acquires after its flag.
+template <class Fail>
+__device__ __forceinline__ void grid_barrier(uint32_t *sync, uint32_t nbar, Fail fail)
+{
+    const uint32_t grp = blockIdx.x % kBarGroups;
+    const uint32_t ng = gridDim.x < kBarGroups ? gridDim.x : kBarGroups;
+    const uint32_t gsz = (gridDim.x - grp + kBarGroups - 1) / kBarGroups;  // workgroups in grp
+    const uint32_t old = __hip_atomic_fetch_add(&sync[kSyncArrive + kSyncLine * grp], 1u,
+                                                __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == nbar * gsz) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const uint32_t top = __hip_atomic_fetch_add(&sync[kSyncTop], 1u, __ATOMIC_RELEASE,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (top + 1 == nbar * ng) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            for (uint32_t g = 0; g < ng; ++g)
+                __hip_atomic_store(&sync[kSyncFlag + kSyncLine * g], nbar, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    uint32_t spins = 0;
+    while (__hip_atomic_load(&sync[kSyncFlag + kSyncLine * grp], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < nbar) {
+        if (++spins == kSpinLimit) {
+            fail();
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
 constexpr int kChainMaxK = 16384;  // 4 stages: a task and the next fit the 8 slots
 
 __host__ __device__ __forceinline__ int chain_stages(int K) { return ((K >> 5) + kStageChunks - 1) / kStageChunks; }
@@ -824,7 +879,9 @@ void gemv_chain_kernel(const ChainArgs a)
         return __hip_atomic_load(&entered[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
                kChainCompute;
     };
-    auto fail = [&]() { __hip_atomic_store(&a.sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto fail = [&]() {
+        __hip_atomic_store(&a.sync[kSyncTimeout], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     // the level table, by every wave
     fill_level_table<FMT, 1024>(tbl);
@@ -947,23 +1004,9 @@ void gemv_chain_kernel(const ChainArgs a)
                     __builtin_amdgcn_s_sleep(1);
                 }
                 if (wait) {
-                    // grid barrier between the loaders: this workgroup's
-                    // outputs are released with the arrival, the others'
-                    // acquired after it
                     ++nbar;
-                    if (lane == 0) {
-                        __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                        const uint32_t target = (uint32_t)nbar * gridDim.x;
-                        uint32_t gspins = 0;
-                        while (__hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                               target) {
-                            if (++gspins == kSpinLimit) {
-                                fail();
-                                break;
-                            }
-                            __builtin_amdgcn_s_sleep(1);
-                        }
-                    }
+                    if (lane == 0)
+                        grid_barrier(a.sync, nbar, fail);
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 }
                 chain_dma_x(T, xb, lane);
@@ -1093,11 +1136,17 @@ void gemv_chain_kernel(const ChainArgs a)
         // the last workgroup to finish leaves the counters at zero for the
         // next chain on this sync buffer (every workgroup is past its last
         // barrier by then)
-        const uint32_t d =
-            __hip_atomic_fetch_add(&a.sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t d = __hip_atomic_fetch_add(&a.sync[kSyncDone], 1u, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
         if (d == gridDim.x - 1) {
-            __hip_atomic_store(&a.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.sync[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            for (int g = 0; g < kBarGroups; ++g) {
+                __hip_atomic_store(&a.sync[kSyncArrive + kSyncLine * g], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.sync[kSyncFlag + kSyncLine * g], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __hip_atomic_store(&a.sync[kSyncTop], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sync[kSyncDone], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -10,8 +10,8 @@
 #include "q4.h"
 #include "q4_internal.hpp"
 
-// The sync words of q4_gemv_chain_static: one chain's grid-barrier
-// arrivals, finished workgroups and timeout flag (Q4_GEMV_CHAIN_SYNC_BYTES),
+// The sync words of q4_gemv_chain_static: one chain's finished-workgroup
+// count, timeout flag and grid-barrier words (Q4_GEMV_CHAIN_SYNC_BYTES),
 // in static device memory that each GPU holds for the life of the process.
 // In host code this name is not a device address; the address of each
 // device's copy comes from hipGetSymbolAddress.
@@ -252,7 +252,7 @@ q4_status q4_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_task *
     q4_status st = check_chain(f, g, act_t, tasks, ntasks);
     if (st != Q4_OK)
         return st;
-    if (!aligned(sync, 16))
+    if (!aligned(sync, 128))
         return Q4_EALIGN;
     return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
 }
@@ -266,9 +266,9 @@ q4_status q4_gemv_chain_static(q4_format f, int g, q4_dtype act_t, const q4_gemv
     uint32_t *sync = nullptr;
     if (scratch_for_current_device(&sync) != hipSuccess)
         return Q4_EHIP;
-    // The kernel leaves the arrival and finish counters (words 0 and 1) at
-    // zero when it ends, as static device memory starts; the timeout flag
-    // (word 2) is sticky and not reported here.
+    // The kernel leaves every word but the timeout flag (word 2) at zero
+    // when it ends, as static device memory starts; the timeout flag is
+    // sticky and not reported here.
     return from_hip(q4::launch_gemv_chain(f, g, act_t, tasks, ntasks, sync, (hipStream_t)stream));
 }
 

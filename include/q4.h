@@ -193,19 +193,19 @@ q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t
  * ntasks is 1..Q4_GEMV_CHAIN_MAX; each K must satisfy K <= Q4_GEMV_CHAIN_MAX_K
  * and each task's codes N*K/2 <= Q4_GEMV_CHAIN_MAX_CODES bytes (else
  * Q4_EUNSUPPORTED); N and K are checked as in q4_gemv.  `sync` is a
- * device buffer of Q4_GEMV_CHAIN_SYNC_BYTES, 16-byte aligned, zeroed by the
- * caller before its first use: the kernel returns words 0 and 1 to zero when
- * it ends, so the buffer can be reused without clearing by later chains on
- * the same stream; chains that may overlap (other streams) need their own.
- * Word 2 becomes nonzero if a wait between tasks gave up after about a second
- * (the grid could not make progress; y is then undefined) and stays set until
- * the caller clears it.  The chain is one launch of one workgroup per
+ * device buffer of Q4_GEMV_CHAIN_SYNC_BYTES, 128-byte aligned, zeroed by the
+ * caller before its first use: the kernel returns every word but word 2 to
+ * zero when it ends, so the buffer can be reused without clearing by later
+ * chains on the same stream; chains that may overlap (other streams) need
+ * their own.  Word 2 becomes nonzero if a wait between tasks gave up after
+ * about a second (the grid could not make progress; y is then undefined) and
+ * stays set until the caller clears it.  The chain is one launch of one workgroup per
  * compute unit, cooperative when a task waits (its grid barrier needs every
  * workgroup resident): a launch the runtime refuses returns Q4_EHIP. */
 #define Q4_GEMV_CHAIN_MAX 64
 #define Q4_GEMV_CHAIN_MAX_K 16384
 #define Q4_GEMV_CHAIN_MAX_CODES 2147483519LL /* 2^31 - 129 */
-#define Q4_GEMV_CHAIN_SYNC_BYTES 16
+#define Q4_GEMV_CHAIN_SYNC_BYTES 2304 /* 18 lines of 128 bytes */
 #define Q4_TASK_NO_WAIT 1u /* x is not written by earlier tasks: no grid-wide wait */
 typedef struct {
     const void *x;        /* [1, K] act_t */

@@ -210,7 +210,7 @@ def test_gemv_task_layout():
     (dict(flags=2), q4.EINVAL),
     (dict(K=16384 + 64), q4.EUNSUPPORTED),       # x no longer fits the LDS buffers
     (dict(N=262144, K=16384), q4.EUNSUPPORTED),   # codes 2 GiB: past Q4_GEMV_CHAIN_MAX_CODES
-    (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),
+    (dict(sync=0x10040), q4.EALIGN),              # sync words need 128 bytes
 ])
 def test_chain_rejects(kw, status):
     assert call_chain(**kw) == status

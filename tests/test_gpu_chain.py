@@ -87,7 +87,7 @@ def test_chain_equals_consecutive_gemv(fmt, act):
             outs = q4.gemv_chain([tuple(t) for t in tasks], sync=sync)
             torch.cuda.synchronize()
             _assert_same(outs, ref, f"{tag} rep{rep}")
-            assert sync.cpu().tolist() == [0, 0, 0, 0], f"{tag}: sync words {sync.cpu().tolist()}"
+            assert not sync.any().item(), f"{tag}: sync words not clear"
 
 
 def test_chain_no_wait_flag():
@@ -137,7 +137,7 @@ def test_chain_slot_reuse(fmt, g, act):
         outs = q4.gemv_chain(tasks, sync=sync)
         torch.cuda.synchronize()
         _assert_same(outs, ref, f"slots fmt{fmt} g{g} rep{rep}")
-        assert sync.cpu().tolist() == [0, 0, 0, 0]
+        assert not sync.any().item()
 
 
 @pytest.mark.parametrize("fmt,g,act", [(q4.NF4, 64, q4.BF16), (q4.INT4_ASYM, 32, q4.F16),
@@ -164,7 +164,7 @@ def test_chain_blocked_rows(fmt, g, act):
             outs = q4.gemv_chain(tasks, sync=sync)
             torch.cuda.synchronize()
             _assert_same(outs, ref, f"blocked chain {ci} fmt{fmt} g{g} rep{rep}")
-            assert sync.cpu().tolist() == [0, 0, 0, 0]
+            assert not sync.any().item()
 
 
 def test_chain_longest():

@@ -83,4 +83,4 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(everything(), ref)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i}"
-        assert sync.cpu().tolist() == [0, 0, 0, 0]
+        assert not sync.any().item()
