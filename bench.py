@@ -17,7 +17,9 @@ token times tokens/s.  Reported beside it: the same chain with a grid-wide
 wait before every product (each reading the previous outputs' memory order),
 and the 128 single-product q4_gemv launches replayed from a HIP graph.
 
-The same run also measures, each with HIP events on the launch stream:
+Also reported for the token: the 128 single-product launches back to back on
+the plain stream.  The same run also measures, each with HIP events on the
+launch stream:
   * the one-shot quantize of all weights (HBM-resident fp16 input),
   * dequantize of a 14336x4096 INT4-asym weight to bf16,
   * the prefill GEMM M=2048, N=14336, K=4096, INT4-asym g32, bf16 x
@@ -28,7 +30,10 @@ The same run also measures, each with HIP events on the launch stream:
   * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
     INT4-sym g128 4096x4096 at M = 1, NF4 g64 11008x4096 and 4096x11008 at
     M = 1, 4, 16,
-  * the CPU oracle on a time-bounded sample of the token (cpu_baseline).
+  * quantize and dequantize of the single-matrix workloads in their own
+    formats on cold buffers,
+  * the CPU oracle on a time-bounded sample of the token, on one thread and
+    on the host's cores (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -70,8 +75,9 @@ def parse():
     p.add_argument("--no-dep", action="store_true",
                    help="skip the chain with a grid-wide wait before every product (its "
                         "cooperative launch; for profiler runs)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="time budget of the CPU-oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="time budget of the CPU-oracle sample (half on one thread, half on "
+                        "all cores)")
     p.add_argument("--skip-extra", action="store_true",
                    help="time only the decode token (for profiler runs)")
     p.add_argument("--only", choices=["gemm", "gemm_dx", "quantize", "dequantize", "copy"],
@@ -214,8 +220,8 @@ def main():
         torch.cuda.synchronize()
         if not all(torch.equal(a, b) for a, b in zip(flat_y, ref)):
             raise RuntimeError(f"{name} chain differs from single-product launches")
-    if sync.cpu().tolist() != [0, 0, 0, 0]:
-        raise RuntimeError(f"chain sync words not clear: {sync.cpu().tolist()}")
+    if sync.any().item():
+        raise RuntimeError("chain sync words not clear")
 
     # the chained launches of the timed steps are separated by events on the
     # launch stream, one before the first and one after each (the kernel's
@@ -248,6 +254,8 @@ def main():
     timed = _timer(torch, stream)
     reps = max(args.steps // 5, 3)
     dep_ms = None if args.no_dep else timed(lambda: run_chains(dep), reps)
+    # the same 128 GEMVs as single launches back to back on the plain stream
+    plain_ms = timed(token_single, reps)
     single_ms = None
     if not args.no_graph:
         side = torch.cuda.Stream()
@@ -283,6 +291,7 @@ def main():
     if not args.skip_extra:
         extra = extra_legs(torch, q4, dev, stream)
         extra["gemv_configs_cold"] = config_gemvs(torch, q4, dev, stream)
+        extra["codec_configs_cold"] = codec_configs(torch, q4, dev, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -315,6 +324,8 @@ def main():
             "dependent_chain_ms_per_step": None if dep_ms is None else round(dep_ms, 4),
             "dependent_chain_GBps": None if dep_ms is None
             else round(w_bytes / (dep_ms * 1e-3) / 1e9, 1),
+            "single_launch_plain_ms_per_step": round(plain_ms, 4),
+            "single_launch_plain_GBps": round(w_bytes / (plain_ms * 1e-3) / 1e9, 1),
             "single_launch_graph_ms_per_step": None if single_ms is None else round(single_ms, 4),
             "single_launch_graph_GBps": None if single_ms is None
             else round(w_bytes / (single_ms * 1e-3) / 1e9, 1),
@@ -475,6 +486,57 @@ def _rotated_gemv(torch, q4, dev, stream, fmt, g, N, K, Ms, act, seed, min_bytes
     return {"weight_bytes": nb, "copies": R, **out}
 
 
+def _codec_rates(torch, q4, dev, stream, fmt, g, N, K, out_dt, seed, mu=0.0,
+                 min_bytes=512 << 20):
+    """Quantize and dequantize GB/s on cold buffers: R copies of the fp16
+    weight and of its quantized form (R * bytes >= 512 MiB, more than the
+    256 MB last-level cache), used in turn; algorithmic bytes = fp16 read +
+    codes and metadata written (quantize), codes and metadata read + N K
+    16-bit values written (dequantize)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w0 = torch.empty((N, K), dtype=torch.float16, device=dev).normal_(mu, 0.02, generator=gen)
+    q0 = q4.quantize(w0, fmt, g)
+    nb = N * K * 2 + q0.nbytes()
+    R = max(2, -(-min_bytes // nb))
+    ws = [w0] + [w0.clone() for _ in range(R - 1)]
+    qs = [q0] + [q4.quantize(w0, fmt, g) for _ in range(R - 1)]
+    outs = [torch.empty((N, K), dtype=out_dt, device=dev) for _ in range(R)]
+    timed = _timer(torch, stream)
+
+    def quant_all():
+        for w, q in zip(ws, qs):
+            q4.quantize(w, fmt, g, out=q)
+
+    def deq_all():
+        for q, o in zip(qs, outs):
+            q4.dequantize(q, out_dt, out=o)
+    qt = timed(quant_all, 3) / R
+    dt = timed(deq_all, 3) / R
+    del ws, qs, outs
+    torch.cuda.empty_cache()
+    return {"copies": R, "bytes": nb,
+            "quantize_us": round(qt * 1e3, 2), "quantize_GBps": round(nb / (qt * 1e-3) / 1e9, 1),
+            "dequantize_us": round(dt * 1e3, 2),
+            "dequantize_GBps": round(nb / (dt * 1e-3) / 1e9, 1)}
+
+
+def codec_configs(torch, q4, dev, stream):
+    """Quantize / dequantize of the single-matrix workloads in their own
+    formats (NF4 g64 1024x1024 -> fp16; INT4-sym g128 4096x4096 -> fp16; NF4
+    g64 11008x4096 -> bf16; INT4-asym g32 14336x4096 -> bf16)."""
+    return {
+        "c1_nf4_g64_1024x1024_f16": _codec_rates(torch, q4, dev, stream, q4.NF4, 64, 1024, 1024,
+                                                 torch.float16, 101),
+        "c2_sym_g128_4096x4096_f16": _codec_rates(torch, q4, dev, stream, q4.INT4_SYM, 128, 4096,
+                                                  4096, torch.float16, 201),
+        "c3_nf4_g64_11008x4096_bf16": _codec_rates(torch, q4, dev, stream, q4.NF4, 64, 11008, 4096,
+                                                   torch.bfloat16, 301),
+        "c4_asym_g32_14336x4096_bf16": _codec_rates(torch, q4, dev, stream, q4.INT4_ASYM, 32,
+                                                    14336, 4096, torch.bfloat16, 401, mu=0.001),
+    }
+
+
 def config_gemvs(torch, q4, dev, stream):
     """The single-matrix GEMV configurations on cold weights: INT4-sym g128
     4096x4096 (fp16 x, M = 1) and the NF4 g64 MLP shapes 11008x4096 and
@@ -562,53 +624,83 @@ def extra_legs(torch, q4, dev, stream):
     }
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float):
-    """The C oracle (single thread) on the token's matrices, layer by layer
-    (the first 2048 rows of each), 64 rows at a time until the time budget
-    is spent: dequantize each weight row to bf16 and form the fp64 product
-    with x, as the reference does.  The weights are drawn with the same seeds
-    and distribution as the GPU run's (a different generator, so not the
-    same bits)."""
-    import numpy as np
+    """The C oracle on the host cores, on a bounded sample of the token: the
+    first 2048 rows of each matrix, layer by layer, in blocks of 64 rows (at
+    most 512 blocks, drawn with the same seeds and distribution as the GPU
+    run's weights but a different generator, so not the same bits), each
+    quantized by the oracle beforehand (not timed).  Timed: dequantize each
+    row to bf16 and form the fp64 product with x, as the reference does --
+    first on one thread, then on T threads (the host's cores, at most 16),
+    each for about half the budget, cycling over the blocks.  The oracle is
+    plain scalar C; ctypes releases the interpreter lock during each call,
+    so the threads run in parallel."""
+    import concurrent.futures as cf
     import oracle
     from bit_group_wise_amd import synth
 
-    rows_done = 0
-    bytes_done = 0
-    t_total = 0.0
+    T = max(1, min(len(os.sched_getaffinity(0)), 16))
     xs = {HID: synth.act_bits(1, HID, 5900, synth.BF16), FFN: synth.act_bits(1, FFN, 5901, synth.BF16)}
-    mats = []
+    specs = []
     for layer in range(LAYERS):
         for name, N, K, parts in LAYER_MATS:
             for part, rows, idx in parts:
-                if t_total >= seconds:
-                    break
-                # the first 2048 rows of each matrix (a row-major draw, so
-                # these are the full matrix's first rows)
-                w = synth.weight_f16_bits(min(rows, 2048), K, seed=5000 + 7 * layer + idx)
-                rows = w.shape[0]
-                row_bytes = K // 2 + (K // 64) * 4
-                for r0 in range(0, rows, 64):
-                    if t_total >= seconds:
-                        break
-                    blk = w[r0:r0 + 64]
-                    codes, scales, _ = oracle.quantize(oracle.NF4, 64, blk)
-                    t = time.perf_counter()
-                    oracle.matmul(oracle.NF4, 64, oracle.BF16, xs[K], codes, scales, None,
-                                  blk.shape[0], K)
-                    t_total += time.perf_counter() - t
-                    rows_done += blk.shape[0]
-                    bytes_done += blk.shape[0] * row_bytes
-                mats.append(f"{part}{layer}")
-        if t_total >= seconds:
-            break
+                for r0 in range(0, min(rows, 2048), 64):
+                    specs.append((f"{part}{layer}", K, 5000 + 7 * layer + idx, r0))
+    specs = specs[:512]
+
+    def prep(spec):
+        name, K, seed, r0 = spec
+        # the first rows of a row-major draw are the full matrix's first rows
+        w = synth.weight_f16_bits(r0 + 64, K, seed=seed)[r0:r0 + 64]
+        codes, scales, _ = oracle.quantize(oracle.NF4, 64, w)
+        return name, K, codes, scales
+
+    with cf.ThreadPoolExecutor(T) as ex:
+        blocks = list(ex.map(prep, specs))
+    row_bytes = {K: K // 2 + (K // 64) * 4 for K in (HID, FFN)}
+
+    def run(block):
+        name, K, codes, scales = block
+        oracle.matmul(oracle.NF4, 64, oracle.BF16, xs[K], codes, scales, None, 64, K)
+        return 64 * row_bytes[K]
+
+    # one thread
+    done1, t0, i = 0, time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds / 2:
+        done1 += run(blocks[i % len(blocks)])
+        i += 1
+    t1 = time.perf_counter() - t0
+    # all T threads, in rounds of 4 T blocks
+    doneT, t0, i = 0, time.perf_counter(), 0
+    with cf.ThreadPoolExecutor(T) as ex:
+        while time.perf_counter() - t0 < seconds / 2:
+            batch = [blocks[(i + j) % len(blocks)] for j in range(4 * T)]
+            i += 4 * T
+            doneT += sum(ex.map(run, batch))
+    tT = time.perf_counter() - t0
     return {
-        "value": round(bytes_done / t_total / 1e9, 4),
+        "value": round(doneT / tT / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": T,
         "kind": "oracle",
-        "sample": f"{rows_done} weight rows (the first 2048 of each of {mats[0]} .. {mats[-1]}), "
-                  f"NF4 g64, M=1 bf16: dequantize + fp64 dot product, {t_total:.1f}s on one thread",
+        "sample": f"{len(blocks)} blocks of 64 weight rows (the first 2048 rows of each of "
+                  f"{blocks[0][0]} .. {blocks[-1][0]}), NF4 g64, M=1 bf16: dequantize + fp64 dot "
+                  f"product, cycled for {tT:.1f}s on {T} threads ({doneT / 2**20:.0f} MiB); "
+                  f"one thread: {done1 / t1 / 1e9:.4f} GB/s over {t1:.1f}s",
+        "value_one_thread": round(done1 / t1 / 1e9, 4),
+        "cpu_model": _cpu_model(),
     }
 
 
