@@ -247,6 +247,9 @@ __device__ __forceinline__ LaneOffs lane_offs(int lane, int gshift)
 // Non-temporal loads: the weights are streamed once per product, so they are
 // not kept in the caches (the "nt" cache-policy bit).
 constexpr int kNT = 2;
+// The device-scope cache policy (the "sc1" bit): the access is coherent
+// across the device's L2 caches, as an agent-scope atomic load is.
+constexpr int kCoherent = 16;
 
 // The loads of stage s of a row.  Each array is read through a view that
 // starts at the stage's first byte and ends at the row's last (built with
@@ -659,58 +662,66 @@ struct ChainArgs {
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded waits (of the order of a second)
 
 // Layout of the sync buffer, in 32-bit words (one 128-byte line holds 32):
-// line 0 the finished-workgroup count and the timeout flag, then the grid
-// barrier's words each on a line of its own so that the atomics and polls
-// of different groups do not contend -- kBarGroups arrival counters, the
-// top-level counter, kBarGroups release flags.
+// line 0 the finished-workgroup count and the timeout flag; lines 1-8 the
+// grid barrier's arrival counters, one per group, each on a line of its own
+// so that the atomics of different groups do not contend; line 9 the
+// groups' done flags, words 0-7 (polled, never the target of an atomic).
 constexpr int kSyncLine = 32;
 constexpr int kBarGroups = 8;
 constexpr int kSyncDone = 0;
 constexpr int kSyncTimeout = 2;
-constexpr int kSyncArrive = kSyncLine;                       // + kSyncLine * group
-constexpr int kSyncTop = kSyncLine * (1 + kBarGroups);
-constexpr int kSyncFlag = kSyncLine * (2 + kBarGroups);      // + kSyncLine * group
-static_assert(4 * (kSyncFlag + kSyncLine * kBarGroups) <= Q4_GEMV_CHAIN_SYNC_BYTES,
-              "sync buffer too small");
+constexpr int kSyncArrive = kSyncLine;                    // + kSyncLine * group
+constexpr int kSyncFlag = kSyncLine * (1 + kBarGroups);  // + group
+static_assert(4 * (kSyncFlag + kSyncLine) == Q4_GEMV_CHAIN_SYNC_BYTES, "sync buffer layout");
 
-// Grid barrier number `nbar` of a chain (one thread per workgroup).  Two
-// levels, so that no counter takes more than a few dozen atomics per
-// barrier: workgroup b arrives at group b % 8's counter; the last arrival
-// of a group arrives at the top counter; the last group's last arrival
-// raises every group's release flag to nbar, and each workgroup polls its
-// own group's flag.  The counters only grow during a chain (barrier n is
-// complete at n times the arrivals), so no barrier resets them.  Each
-// arrival releases its workgroup's outputs; a group's last arrival
-// acquires the others' before it passes them on (release sequence on the
-// counter, then an acquire fence), and the caller acquires after its flag.
+// Grid barrier number `nbar` of a chain, run by one whole wave per
+// workgroup.  Workgroup b arrives at group b % 8's counter; the group's last
+// arrival raises the group's done flag to nbar; lane g of every waiting wave
+// polls group g's flag until all are up.  Arrivals are spread over 8
+// counters so that no counter takes more than a few dozen atomics per
+// barrier, and the polls read a line no atomic targets.  The counters only
+// grow during a chain (barrier n is complete at n times the arrivals), so no
+// barrier resets them.
+//
+// Memory order without cache maintenance.  Every access that carries data
+// from one workgroup to another -- the outputs of a task that a later task
+// reads, and that read itself -- is an agent-scope coherent access (the
+// device-scope cache policy, sc1, that agent-scope atomic loads and stores
+// use), so no dirty or stale copy of it sits in any one XCD's L2.  What is
+// left is order: a compute wave waits for its output stores to complete
+// (s_waitcnt vmcnt(0)) before it counts into the next task in LDS; the
+// loader arrives only after every compute wave has; the last arrival of a
+// group and the flag store follow the counter's atomic return; the x
+// loads go out after a flag poll has returned.  Each step starts after the
+// previous one has completed, so the outputs are at the coherence point
+// before any reader asks for them.  (A release/acquire fence pair at agent
+// scope would write back and invalidate the L2 at every barrier: measured
+// at about 4 us per barrier on the 7B token's chain.)
 template <class Fail>
-__device__ __forceinline__ void grid_barrier(uint32_t *sync, uint32_t nbar, Fail fail)
+__device__ __forceinline__ void grid_barrier(uint32_t *sync, uint32_t nbar, int lane, Fail fail)
 {
-    const uint32_t grp = blockIdx.x % kBarGroups;
     const uint32_t ng = gridDim.x < kBarGroups ? gridDim.x : kBarGroups;
-    const uint32_t gsz = (gridDim.x - grp + kBarGroups - 1) / kBarGroups;  // workgroups in grp
-    const uint32_t old = __hip_atomic_fetch_add(&sync[kSyncArrive + kSyncLine * grp], 1u,
-                                                __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == nbar * gsz) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const uint32_t top = __hip_atomic_fetch_add(&sync[kSyncTop], 1u, __ATOMIC_RELEASE,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (top + 1 == nbar * ng) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            for (uint32_t g = 0; g < ng; ++g)
-                __hip_atomic_store(&sync[kSyncFlag + kSyncLine * g], nbar, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) {
+        const uint32_t grp = blockIdx.x % kBarGroups;
+        const uint32_t gsz = (gridDim.x - grp + kBarGroups - 1) / kBarGroups;  // its workgroups
+        const uint32_t old = __hip_atomic_fetch_add(&sync[kSyncArrive + kSyncLine * grp], 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old + 1 == nbar * gsz)
+            __hip_atomic_store(&sync[kSyncFlag + grp], nbar, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
+    const uint32_t g = (uint32_t)lane < ng ? (uint32_t)lane : 0u;
     uint32_t spins = 0;
-    while (__hip_atomic_load(&sync[kSyncFlag + kSyncLine * grp], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT) < nbar) {
+    while (!__all(__hip_atomic_load(&sync[kSyncFlag + g], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) >= nbar)) {
         if (++spins == kSpinLimit) {
             fail();
             break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 constexpr int kChainMaxK = 16384;  // 4 stages: a task and the next fit the 8 slots
 
@@ -811,6 +822,7 @@ constexpr int kChainDmaAhead = 40;
 // The whole offset is the lane's (voffset, range-checked against the x
 // view), so pieces past K read zeros: the stored rows are padded to whole
 // stages with zeros.
+template <int CPOL = 0>
 __device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int lane)
 {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(T.x, (int64_t)T.K * 2);
@@ -824,7 +836,7 @@ __device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int l
             for (int j = 0; j < 4; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xr, (__attribute__((address_space(3))) void *)(xb + chain_x_index(slot, j, 64 * h)),
-                    16, 64 * (kStageChunks * s + 64 * h + lane) + 16 * j, 0, 0, 0);
+                    16, 64 * (kStageChunks * s + 64 * h + lane) + 16 * j, 0, 0, CPOL);
     }
 }
 
@@ -1004,12 +1016,11 @@ void gemv_chain_kernel(const ChainArgs a)
                     __builtin_amdgcn_s_sleep(1);
                 }
                 if (wait) {
-                    ++nbar;
-                    if (lane == 0)
-                        grid_barrier(a.sync, nbar, fail);
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    grid_barrier(a.sync, ++nbar, lane, fail);
+                    chain_dma_x<kCoherent>(T, xb, lane);  // earlier outputs
+                } else {
+                    chain_dma_x(T, xb, lane);
                 }
-                chain_dma_x(T, xb, lane);
                 issued = t + 1;
             }
             issue_ahead();
@@ -1036,8 +1047,11 @@ void gemv_chain_kernel(const ChainArgs a)
         // first (the loader releases them to the grid).
         auto enter = [&]() {
             const int t = ++cur;
-            if (DEP && ctl_wait(task(t).ctl))
+            if (DEP && ctl_wait(task(t).ctl)) {
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 wait_vm<0>();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
             if (lane == 0)
                 __hip_atomic_fetch_add(&entered[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             uint32_t spins = 0;
@@ -1115,11 +1129,16 @@ void gemv_chain_kernel(const ChainArgs a)
                     if (cp.s == S - 1) {
                         const float out = diag_sum(acc[0], lane);
                         acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        if (cp.row < end && lane == 0)
-                            // through a global (not flat) pointer: a flat store
-                            // may write LDS, so LDS reads after it would wait
-                            *(__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row) =
-                                (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                        // through a global (not flat) pointer: a flat store
+                        // may write LDS, so LDS reads after it would wait
+                        auto *const yp = (__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row);
+                        const uint16_t yb = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
+                        if (cp.row < end && lane == 0) {
+                            if constexpr (DEP)  // later tasks may read it (coherent store)
+                                __hip_atomic_store(yp, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                *yp = yb;
+                        }
                     }
                     pos[q] = advance(pos[(q + P - 1) % P]);
                     load_pos(st[q], pos[q]);
@@ -1142,10 +1161,9 @@ void gemv_chain_kernel(const ChainArgs a)
             for (int g = 0; g < kBarGroups; ++g) {
                 __hip_atomic_store(&a.sync[kSyncArrive + kSyncLine * g], 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.sync[kSyncFlag + kSyncLine * g], 0u, __ATOMIC_RELAXED,
+                __hip_atomic_store(&a.sync[kSyncFlag + g], 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
-            __hip_atomic_store(&a.sync[kSyncTop], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.sync[kSyncDone], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }

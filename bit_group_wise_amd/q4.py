@@ -38,7 +38,7 @@ SIGNATURES = {
 }
 
 # q4_gemv_chain limits and the task record (layout of q4_gemv_task)
-CHAIN_MAX, CHAIN_MAX_K, CHAIN_SYNC_BYTES, TASK_NO_WAIT = 64, 16384, 2304, 1
+CHAIN_MAX, CHAIN_MAX_K, CHAIN_SYNC_BYTES, TASK_NO_WAIT = 64, 16384, 1280, 1
 
 
 class GemvTask(ctypes.Structure):

@@ -205,7 +205,7 @@ q4_status q4_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, int64_t
 #define Q4_GEMV_CHAIN_MAX 64
 #define Q4_GEMV_CHAIN_MAX_K 16384
 #define Q4_GEMV_CHAIN_MAX_CODES 2147483519LL /* 2^31 - 129 */
-#define Q4_GEMV_CHAIN_SYNC_BYTES 2304 /* 18 lines of 128 bytes */
+#define Q4_GEMV_CHAIN_SYNC_BYTES 1280 /* 10 lines of 128 bytes */
 #define Q4_TASK_NO_WAIT 1u /* x is not written by earlier tasks: no grid-wide wait */
 typedef struct {
     const void *x;        /* [1, K] act_t */

@@ -7,7 +7,8 @@ activation dtype; ragged K (a partial last stage), K of several stages up to
 the largest supported, tasks with fewer rows than the grid has waves (most
 waves skip them), a task whose x is an earlier task's y (the grid-wide wait),
 the Q4_TASK_NO_WAIT flag, the longest chain, and reuse of the sync buffer
-(the kernel leaves its counters at zero and sets no timeout flag).  One chain
+(the kernel leaves its counters at zero and sets no timeout flag), and
+chains of dependent tasks rerun into the same buffers.  One chain
 is also checked against the fp64 oracle within the product tolerance.
 """
 
@@ -184,6 +185,34 @@ def test_chain_longest():
     torch.cuda.synchronize()
     _assert_same(outs, ref, "longest")
     assert torch.isfinite(outs[-1].float()).all()
+
+
+@pytest.mark.parametrize("fmt,g,act", [(q4.NF4, 64, q4.BF16), (q4.INT4_ASYM, 32, q4.F16)])
+def test_chain_dependent_reuse(fmt, g, act):
+    """Tasks that each read the previous task's output, run again and again
+    into the same output buffers with a new first input each time: a read
+    of an output before it was written (a copy left from the previous run,
+    held in some XCD's L2 by a kernel that read the buffers in between)
+    would give the previous run's bits."""
+    dims = [4096, 4096, 11008, 4096, 2176, 4096]
+    qs = [_weight(n, k, fmt, g, 9500 + i, sigma=k ** -0.5) for i, (k, n) in
+          enumerate(zip(dims[:-1], dims[1:]))]
+    ys = [torch.empty((1, q.N), dtype=TORCH_ACT[act], device=DEV) for q in qs]
+    sync = q4.chain_sync(DEV)
+    for rep in range(4):
+        x0 = _x(dims[0], act, 9600 + rep)
+        tasks = [(x0 if i == 0 else ys[i - 1], q, ys[i]) for i, q in enumerate(qs)]
+        # pull the previous run's outputs into the L2s of the XCDs that run
+        # a reduction over them
+        _ = [float(y.float().sum()) for y in ys]
+        outs = q4.gemv_chain(tasks, sync=sync)
+        ref, x = [], x0
+        for q in qs:
+            x = q4.gemv(x, q)
+            ref.append(x)
+        torch.cuda.synchronize()
+        _assert_same(outs, ref, f"dependent reuse fmt{fmt} rep{rep}")
+        assert not sync.any().item()
 
 
 def test_chain_against_oracle():
