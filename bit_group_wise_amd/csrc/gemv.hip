@@ -1041,12 +1041,13 @@ void gemv_chain_kernel(const ChainArgs a)
         const LaneOffs lo = lane_offs<FMT>(lane, a.gshift);
         const int total_waves = gridDim.x * kChainCompute;
         __syncthreads();  // the table, the counters and x of task tlo
-        int cur = tlo;
-        // Entering task cur + 1: count in, then wait for its x.  Before a
-        // task that reads earlier outputs, this wave's own stores complete
-        // first (the loader releases them to the grid).
-        auto enter = [&]() {
-            const int t = ++cur;
+        int cur = tlo;  // the last task this wave has counted into
+        // Counting into task t (this wave is done with every earlier task).
+        // Before a task that reads earlier outputs, this wave's own stores
+        // complete first (the loader then passes them on to the grid): with
+        // the count taken before the task's first weight loads go out, the
+        // wait covers the stores alone.
+        auto arrive = [&](int t) {
             if (DEP && ctl_wait(task(t).ctl)) {
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 wait_vm<0>();
@@ -1054,6 +1055,9 @@ void gemv_chain_kernel(const ChainArgs a)
             }
             if (lane == 0)
                 __hip_atomic_fetch_add(&entered[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
+        // Waiting for x of task t in its slots.
+        auto await_x = [&](int t) {
             uint32_t spins = 0;
             while (__hip_atomic_load(&ready[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 1) {
                 if (++spins == kSpinLimit) {
@@ -1084,8 +1088,10 @@ void gemv_chain_kernel(const ChainArgs a)
                 step = total_waves;
                 end = tv.N;
             }
+            while (cur < t)
+                arrive(++cur);
             if (first >= end)
-                continue;  // no rows here (the task is still entered below or at the end)
+                continue;  // no rows here
             const int S = tv.S;
             // positions: rows first, first + step, ...; a row at or past end
             // loads from an empty view (zeros) and stores nothing
@@ -1110,8 +1116,7 @@ void gemv_chain_kernel(const ChainArgs a)
                     pos[q] = advance(pos[q - 1]);
                 load_pos(st[q], pos[q]);
             }
-            while (cur < t)
-                enter();
+            await_x(t);
             if (S == 1)
                 chain_x_slice(xreg, xb, tv.xbase, 0, lane);
             // A round of the ring is never left in the middle (the load
@@ -1147,7 +1152,7 @@ void gemv_chain_kernel(const ChainArgs a)
         }
         // waves with no rows in the last tasks still count into them
         while (cur < thi)
-            enter();
+            arrive(++cur);
     }
     wait_vm<0>();  // no LDS DMA may be in flight when the workgroup ends
     __syncthreads();
