@@ -81,7 +81,10 @@ __device__ __forceinline__ View make_view(const void *base, int64_t bytes)
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t at(const View &v, uint32_t off)
 {
-    const uint32_t n = off < v.bytes ? v.bytes - off : 0u;
+    // (read back as a wave-uniform value: the compiler forms this clamped
+    // difference with a vector instruction, and a resource it cannot prove
+    // uniform turns every load through it into a loop over lanes)
+    const uint32_t n = __builtin_amdgcn_readfirstlane(off < v.bytes ? v.bytes - off : 0u);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(v.base + off), (short)0, (int)n,
                                              0x00020000);
 }

@@ -58,7 +58,10 @@ static_assert(TN * TK / 16 == kBlock, "16 columns of one row per thread");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dx_rsrc(const void *base, int64_t bytes)
 {
-    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)bytes);
+    // (read back as a wave-uniform value: a resource the compiler cannot
+    // prove uniform turns every load through it into a loop over lanes)
+    const uint32_t n = __builtin_amdgcn_readfirstlane(
+        bytes <= 0 ? 0u : (bytes >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)bytes));
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
                                              0x00020000);
 }
