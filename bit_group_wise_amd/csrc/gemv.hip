@@ -106,18 +106,26 @@ __device__ __forceinline__ float level_of(int i, float lane_entry)
 }
 
 // Fill the table: `block` threads, thread t writes pieces t, t + block, ...
+// Piece p holds entry p >> 4, so thread t's pieces share the entry's low
+// nibble ((t >> 4) & 15: block is a multiple of 256) and their high nibbles
+// ((t >> 8) + i block / 256) are the same across the wave: one lane
+// permute for the low level, a read of one lane for each high level.
 template <int FMT, int BLOCK>
 __device__ __forceinline__ void fill_level_table(uint32_t *tbl)
 {
-    static_assert(kTablePieces % BLOCK == 0, "whole rounds of pieces");
+    static_assert(kTablePieces % BLOCK == 0 && BLOCK % 256 == 0, "whole rounds of pieces");
     const float mine = level_fmt(FMT) == Q4_NF4 ? nf4_lane_entry<FMT>() : 0.0f;
+    const uint32_t lo = std::bit_cast<uint32_t>(level_of<FMT>((threadIdx.x >> 4) & 15, mine));
+    const int h0 = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
 #pragma unroll
     for (int i = 0; i < kTablePieces / BLOCK; ++i) {
-        const int piece = threadIdx.x + BLOCK * i;
-        const int e = piece >> 4;  // 16 pieces of 16 bytes per 256-byte entry
-        const uint32_t lo = std::bit_cast<uint32_t>(level_of<FMT>(e & 15, mine));
-        const uint32_t hi = std::bit_cast<uint32_t>(level_of<FMT>(e >> 4, mine));
-        ((u32x4 *)tbl)[piece] = u32x4{lo, hi, lo, hi};
+        const int hn = h0 + (BLOCK >> 8) * i;  // wave-uniform
+        uint32_t hi;
+        if constexpr (level_fmt(FMT) == Q4_NF4)
+            hi = (uint32_t)__builtin_amdgcn_readlane(std::bit_cast<int>(mine), hn);
+        else
+            hi = std::bit_cast<uint32_t>((float)(FMT == Q4_INT4_SYM ? hn - 8 : hn));
+        ((u32x4 *)tbl)[threadIdx.x + BLOCK * i] = u32x4{lo, hi, lo, hi};
     }
 }
 
@@ -585,8 +593,11 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const Pos cp = pos[q];
-            compute_stage<FMT, ACT, MT, XS>(st[q], acc, tbl, xs, xreg, xr, K, xrow, cp.s, lane, C,
-                                           laneoff, gshift);
+            // (a position past the last row is not computed: its slot is
+            // still refilled below)
+            if (cp.row < N)
+                compute_stage<FMT, ACT, MT, XS>(st[q], acc, tbl, xs, xreg, xr, K, xrow, cp.s, lane,
+                                               C, laneoff, gshift);
             // (double quantization: keep the refill after the compute, which
             // the scheduler otherwise hoists at the cost of registers)
             if constexpr (FMT == Q4_NF4_DQ)
@@ -597,7 +608,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 load_stage<FMT>(st[q], row_ref<FMT>(codes, scales, zeros, pos[q].row, N, row_bytes, G),
                                 pos[q].s, lo, row_bytes, G, gshift);
             }
-            if (cp.s == S - 1) {
+            if (cp.s == S - 1 && cp.row < N) {
                 float out = 0.0f;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
@@ -606,7 +617,7 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                     if (lane == m)
                         out = t;
                 }
-                if (cp.row < N && lane < M && lane < MT)
+                if (lane < M && lane < MT)
                     y[(int64_t)lane * N + cp.row] =
                         (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
             }
@@ -1125,20 +1136,24 @@ void gemv_chain_kernel(const ChainArgs a)
 #pragma unroll
                 for (int q = 0; q < P; ++q) {
                     const Pos cp = pos[q];
-                    if (S > 1)
-                        chain_x_slice(xreg, xb, tv.xbase, cp.s, lane);
-                    // (x comes from registers: no x view, K or chunk count needed)
-                    compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
-                                                      make_rsrc(nullptr, 0), 0, 0, cp.s, lane, 0,
-                                                      laneoff, a.gshift);
-                    if (cp.s == S - 1) {
+                    // (a position past the segment's last row is not
+                    // computed: its slot is still refilled below)
+                    if (cp.row < end) {
+                        if (S > 1)
+                            chain_x_slice(xreg, xb, tv.xbase, cp.s, lane);
+                        // (x comes from registers: no x view, K or chunk count needed)
+                        compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
+                                                          make_rsrc(nullptr, 0), 0, 0, cp.s, lane,
+                                                          0, laneoff, a.gshift);
+                    }
+                    if (cp.s == S - 1 && cp.row < end) {
                         const float out = diag_sum(acc[0], lane);
                         acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                         // through a global (not flat) pointer: a flat store
                         // may write LDS, so LDS reads after it would wait
                         auto *const yp = (__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row);
                         const uint16_t yb = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
-                        if (cp.row < end && lane == 0) {
+                        if (lane == 0) {
                             if constexpr (DEP)  // later tasks may read it (coherent store)
                                 __hip_atomic_store(yp, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             else
