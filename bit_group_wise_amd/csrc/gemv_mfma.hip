@@ -159,10 +159,12 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < kSkRing; ++i) {
             SkStep<FMT, RB> &st = ring[i];
-            // every path computes (a step past the end has zero codes,
-            // scales and x), so the load waits stay partial
+            // a step past the end is not computed (its slot is still
+            // refilled below, so the load waits stay partial)
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
+                if (step + kSkWaves * i >= nsteps)
+                    break;
                 float s, bias;
                 if constexpr (FMT == Q4_NF4) {
                     s = std::bit_cast<float>(st.sraw[b]);
@@ -235,8 +237,11 @@ hipError_t launch_sk_rb(q4_dtype act_t, const void *x, int M, const uint8_t *cod
     return hipGetLastError();
 }
 
-// Row blocks per workgroup: as many (up to 4) as keep at least one
-// workgroup per compute unit, so that x is read once for several blocks.
+// Row blocks per workgroup: the blocks spread over the compute units
+// (ceil(blocks / units), at most 4), so that no unit holds more than its
+// share and x is read once for several blocks.  (With a number of
+// workgroups between one and two per unit, the units holding two finish
+// last: 688 blocks as 344 pairs ran a third longer than as 230 triples.)
 template <int FMT>
 hipError_t launch_sk_fmt(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
                          const void *scales, const uint8_t *zeros, int64_t N, int64_t K,
@@ -244,9 +249,12 @@ hipError_t launch_sk_fmt(q4_dtype act_t, const void *x, int M, const uint8_t *co
 {
     const int64_t nb = (N + 15) / 16;
     const int64_t cus = device_cu_count();
-    if (nb >= 4 * cus)
+    const int64_t rb = (nb + cus - 1) / cus;
+    if (rb >= 4)
         return launch_sk_rb<FMT, 4>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
-    if (nb >= 2 * cus)
+    if (rb == 3)
+        return launch_sk_rb<FMT, 3>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
+    if (rb == 2)
         return launch_sk_rb<FMT, 2>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
     return launch_sk_rb<FMT, 1>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
 }
