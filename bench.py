@@ -80,10 +80,13 @@ def parse():
                         "all cores)")
     p.add_argument("--skip-extra", action="store_true",
                    help="time only the decode token (for profiler runs)")
-    p.add_argument("--only", choices=["gemm", "gemm_dx", "quantize", "dequantize", "copy"],
+    p.add_argument("--only", choices=["gemm", "gemm_dx", "quantize", "dequantize", "copy",
+                                      "gemv_configs", "codec_configs"],
                    help="run one leg alone, a few times, and print its timing "
                         "(for profiler runs); 'copy' is a plain 1 GiB device copy, the "
-                        "reference for scaling HBM byte counters")
+                        "reference for scaling HBM byte counters; 'gemv_configs' and "
+                        "'codec_configs' are the single-matrix GEMV and quantize / "
+                        "dequantize workloads on cold weights")
     return p.parse_args()
 
 
@@ -399,6 +402,10 @@ def one_leg(leg, torch, q4, dev, stream):
         ms = timed(lambda: b.copy_(a), 5)
         return {"leg": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
                 "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    if leg == "gemv_configs":
+        return {"leg": leg, **config_gemvs(torch, q4, dev, stream)}
+    if leg == "codec_configs":
+        return {"leg": leg, **codec_configs(torch, q4, dev, stream)}
     w, x, q = _prefill_inputs(torch, q4, dev)
     N, K = w.shape
     M = x.shape[0]
