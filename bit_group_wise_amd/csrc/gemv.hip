@@ -28,20 +28,24 @@
 //    a pair of 16-bit weights.  The table is replicated per 32 lane slots (a
 //    lane reads only its own banks) and a byte's LDS address is one
 //    v_perm_b32 (code byte -> address bits 8..15, lane slot -> bits 3..7).
-//  * Multiply-accumulate on the matrix cores: a lane's 8 weights of one
-//    code dword and its own 8 activations form its share of a
-//    v_mfma_f32_16x16x32 (weights as the first operand, activations as the
-//    second).  Output (n, n) of that product sums the four lanes n, n + 16,
-//    n + 32, n + 48 of the same row position, so the diagonal of the 16 x 16
-//    accumulator holds the row's partial sums (the rest is never read); the
-//    vector ALUs only dequantize.  M = 2 runs one product per activation row.
+//  * Multiply-accumulate on the matrix cores, as lane-own dot products: in
+//    v_mfma_f32_4x4x4_16b (16 independent 4 x 4 x 4 blocks, block b on lanes
+//    4b .. 4b + 3) lane 4b + i holds row i of the first operand and column
+//    i of the second, so output (i, i) of block b -- register i of lane
+//    4b + i -- is the dot product of that lane's own 4 weights and 4
+//    activations; the other outputs are never read.  A code dword (8
+//    weights) takes two of them per activation row.  (The 16 x 16 x 32
+//    product with the same diagonal use does 4 times the multiply-adds for
+//    the same sums; the chip runs the weight stream at the power limit, and
+//    the smaller product measured 2-4 % faster.)  The vector ALUs only
+//    dequantize.  M = 2 runs one product per activation row.
 //  * Activations: for M = 1 and rows that fit one stage (K <= 4096) each lane
 //    keeps its slices in registers; else, for M <= 2, they are staged once
 //    per workgroup in LDS (rows padded to whole stages with zeros, 16 bytes
 //    of skew per 64-byte chunk so the 16-byte reads of a wave do not collide
 //    in banks); larger K reads them from L2 step by step.
-//  * At the end of a row the diagonal entries are summed across the wave
-//    with DPP; y is rounded once to the activation dtype.
+//  * At the end of a row each lane's own sum (register lane % 4) is summed
+//    across the wave with DPP; y is rounded once to the activation dtype.
 //  * NF4 with double-quantized absmax ("Loading a model in 4-bit", "Where
 //    the accuracy goes"): a chunk's scale is read as its group's 8-bit code
 //    (one byte) and its run's binary32 constant (a dword that the 8 to 32
@@ -337,18 +341,14 @@ __device__ __forceinline__ void load_x(u32x4 (&xv)[MT], const uint32_t *xs,
     }
 }
 
-// Sum of the diagonal of a lane-own-dot 16 x 16 accumulator: entry (n, n)
-// is register n % 4 of lane n + 16 (n / 4), i.e. of the lanes whose
-// position in their 16-lane row is in quad (lane / 16).  Every lane gets
-// the total.  (Selects by per-lane conditions, so no branch: the other
-// entries may hold anything, Inf included, and never reach the sum.)
+// Sum over the wave of the lanes' own dot products: lane l's is register
+// l % 4 of its accumulator (output (i, i) of its 4 x 4 block).  Every lane
+// gets the total.  (Selects by per-lane conditions, so no branch.)
 __device__ __forceinline__ float diag_sum(const f32x4 &a, int lane)
 {
     const float a01 = (lane & 1) ? a[1] : a[0];
     const float a23 = (lane & 1) ? a[3] : a[2];
-    float d = (lane & 2) ? a23 : a01;
-    d = ((lane & 15) >> 2) == (lane >> 4) ? d : 0.0f;
-    return wave_sum(d);
+    return wave_sum((lane & 2) ? a23 : a01);
 }
 
 // Table lookups of one code dword: the binary32 level pairs of its 4 bytes.
@@ -366,8 +366,8 @@ __device__ __forceinline__ void lookup4(uint32_t w, uint32_t laneoff, const uint
 // Products of one stage: 8 steps of 8 weights (two chunks x four dwords of
 // codes).  Per code byte: its LDS address by one v_perm, one 8-byte table
 // read (the two nibbles' binary32 levels), two fma with the chunk's scale
-// and bias and one packed conversion to the activation dtype; per dword one
-// matrix-core product per activation row.  The lookups of the next dword
+// and bias and one packed conversion to the activation dtype; per dword two
+// 4 x 4 x 4 matrix-core products per activation row.  The lookups of the next dword
 // are issued before the current one is converted (scheduling barriers keep
 // that order), so a table read's latency hides behind a dword of
 // arithmetic.
@@ -451,7 +451,7 @@ __device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[m] = mfma<ACT>(wf, xv[m], acc[m]);
+            acc[m] = own_dot8<ACT>(wf, xv[m], acc[m]);
         if (t < 7) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
