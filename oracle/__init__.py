@@ -1,4 +1,5 @@
-"""CPU oracle for 4-bit group-wise weight quantization (NF4, INT4-sym, INT4-asym).
+"""CPU oracle for 4-bit group-wise weight quantization (NF4, INT4-sym, INT4-asym,
+NF4 with double-quantized absmax, FP4).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` import this package.  The product library
@@ -40,9 +41,10 @@ import threading
 
 import numpy as np
 
-NF4, INT4_SYM, INT4_ASYM, NF4_DQ = 0, 1, 2, 3
+NF4, INT4_SYM, INT4_ASYM, NF4_DQ, FP4 = 0, 1, 2, 3, 4
 F16, BF16 = 0, 1
-FORMAT_NAMES = {NF4: "nf4", INT4_SYM: "int4_sym", INT4_ASYM: "int4_asym", NF4_DQ: "nf4_dq"}
+FORMAT_NAMES = {NF4: "nf4", INT4_SYM: "int4_sym", INT4_ASYM: "int4_asym", NF4_DQ: "nf4_dq",
+                FP4: "fp4"}
 DQ_BLOCK = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
             L.orc_dq_s2_offset.restype = _i64
             L.orc_nf4_nearest.argtypes = [ctypes.c_float]
             L.orc_nf4_nearest.restype = _int
+            L.orc_fp4_nearest.argtypes = [ctypes.c_float]
+            L.orc_fp4_nearest.restype = _int
             L.orc_f32_to_f16_array.argtypes = [_f32p, _u16p, _i64]
             L.orc_f16_to_f32_array.argtypes = [_u16p, _f32p, _i64]
             L.orc_f32_to_bf16_array.argtypes = [_f32p, _u16p, _i64]
@@ -119,6 +123,18 @@ def nf4_table() -> np.ndarray:
     """The oracle's codebook, as float32[16]."""
     arr = (ctypes.c_float * 16).in_dll(lib(), "orc_nf4_table")
     return np.array(arr, dtype=np.float32)
+
+
+def fp4_table() -> np.ndarray:
+    """The oracle's FP4 codebook (a reading; parity unpinned against the
+    pages), as float32[16]."""
+    arr = (ctypes.c_float * 16).in_dll(lib(), "orc_fp4_table")
+    return np.array(arr, dtype=np.float32)
+
+
+def fp4_nearest(x: float) -> int:
+    """Nearest FP4 index of a binary32 value (ties to the lower index)."""
+    return int(lib().orc_fp4_nearest(float(np.float32(x))))
 
 
 def f32_to_f16_bits(a) -> np.ndarray:
@@ -183,7 +199,7 @@ def quantize(fmt: int, g: int, w_bits: np.ndarray):
     """Quantize fp16 weights given as uint16 bit patterns [N, K].
 
     Returns (codes uint8[N, K/2], scales, zeros) where scales is float32[N, K/g]
-    for NF4, uint16 fp16 bits [N, K/g] for INT4 and, for NF4_DQ, the flat
+    for NF4 and FP4, uint16 fp16 bits [N, K/g] for INT4 and, for NF4_DQ, the flat
     uint8 buffer of dq_scales_size(N*K/g) bytes (see dq_split); zeros is uint8
     [ceil(N*K/g/2)] for INT4-asym, else None."""
     _check_g(g)
@@ -196,7 +212,7 @@ def quantize(fmt: int, g: int, w_bits: np.ndarray):
     if fmt == NF4_DQ:
         scales = np.zeros(dq_scales_size(N * G), dtype=np.uint8)
     else:
-        scales = np.zeros((N, G), dtype=np.float32 if fmt == NF4 else np.uint16)
+        scales = np.zeros((N, G), dtype=np.float32 if fmt in (NF4, FP4) else np.uint16)
     zeros = np.zeros(((N * G + 1) // 2,), dtype=np.uint8) if fmt == INT4_ASYM else None
     rc = lib().orc_quantize(fmt, g, _p(w, _u16p), N, K, _p(codes, _u8p),
                             scales.ctypes.data_as(_vp),

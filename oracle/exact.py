@@ -78,6 +78,28 @@ def nf4_nearest(x: Fr) -> int:
     return dists.index(best)
 
 
+def e2m1_value(code: int) -> Fr:
+    """The E2M1 element value of a 4-bit code: bit 3 the sign, bits 2..1 the
+    exponent e, bit 0 the mantissa m; m/2 for e = 0, else 2^(e-1) (1 + m/2)."""
+    sign = -1 if code & 8 else 1
+    e, m = (code >> 1) & 3, code & 1
+    mag = Fr(m, 2) if e == 0 else Fr(2) ** (e - 1) * (1 + Fr(m, 2))
+    return sign * mag
+
+
+# FP4 codebook (a reading; the pages name the format without a table): the
+# E2M1 values divided by 6, each the nearest binary32.  The sign of zero is
+# not a Fraction property: code 8 is -0 (checked by the tests separately).
+FP4_TABLE = [rn32(e2m1_value(c) / 6) for c in range(16)]
+
+
+def fp4_nearest(x: Fr) -> int:
+    """Brute force over the 16 entries; a tie keeps the lower index."""
+    dists = [abs(x - q) for q in FP4_TABLE]
+    best = min(dists)
+    return dists.index(best)
+
+
 def nearest_int_level(x: Fr, lo: int, hi: int) -> int:
     """Brute force over the integer levels lo..hi: nearest to x, ties to the
     even level."""
@@ -92,10 +114,15 @@ def nearest_int_level(x: Fr, lo: int, hi: int) -> int:
 def quantize_group(fmt: int, w_bits: list[int]):
     """Exact codes of one group (list of fp16 bit patterns).
 
-    fmt: 0 NF4, 1 INT4-sym, 2 INT4-asym.  Returns (nibbles, scale, zero) where
+    fmt: 0 NF4, 1 INT4-sym, 2 INT4-asym, 4 FP4.  Returns (nibbles, scale, zero) where
     scale is an exact Fraction (the stored binary32 absmax or binary16 scale)
     and zero is the asym zero-point (None otherwise)."""
     w = [f16_value(b) for b in w_bits]
+    if fmt == 4:
+        c = max(abs(v) for v in w)
+        if c == 0:
+            return [0] * len(w), c, None
+        return [fp4_nearest(rn32(v / c)) for v in w], c, None
     if fmt == 0:
         c = max(abs(v) for v in w)
         if c == 0:

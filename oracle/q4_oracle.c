@@ -20,6 +20,20 @@ const float orc_nf4_table[16] = {
     -1.0f,  -0.696f, -0.525f, -0.395f, -0.284f, -0.185f, -0.091f, 0.0f,
     0.079f, 0.161f,  0.246f,  0.338f,  0.441f,  0.562f,  0.720f,  1.0f};
 
+/* The FP4 codebook (a reading: [hf4] "Developer" names the fp4 quant type
+ * beside nf4 but prints no table).  Code bits: bit 3 the sign, bits 2..1 an
+ * exponent e, bit 0 a mantissa bit m, as in the E2M1 element format: the
+ * magnitude is m / 2 for e = 0 and 2^(e-1) (1 + m / 2) otherwise, i.e. 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6.  Divided by 6 so that the largest magnitude is 1
+ * and the block absmax scales it, as NF4's table; each value the nearest
+ * binary32 of the exact fraction (code 8 is -0).  PARITY UNPINNED against
+ * the pages; the tests pin it to the E2M1 definition. */
+const float orc_fp4_table[16] = {
+    0.0f,  (float)(1.0 / 12.0),  (float)(1.0 / 6.0),  0.25f,
+    (float)(1.0 / 3.0),  0.5f,  (float)(2.0 / 3.0),  1.0f,
+    -0.0f, -(float)(1.0 / 12.0), -(float)(1.0 / 6.0), -0.25f,
+    -(float)(1.0 / 3.0), -0.5f, -(float)(2.0 / 3.0), -1.0f};
+
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 / bfloat16 conversions from the format definitions.        */
 
@@ -121,6 +135,22 @@ int orc_nf4_nearest(float x)
     return best;
 }
 
+/* The same rule over the FP4 table: x = 0 (and anything nearer to 0 than to
+ * +-1/12) takes code 0, the lower index of the tie between +0 and -0. */
+int orc_fp4_nearest(float x)
+{
+    int best = 0;
+    double bestd = fabs((double)x - (double)orc_fp4_table[0]);
+    for (int i = 1; i < 16; ++i) {
+        double d = fabs((double)x - (double)orc_fp4_table[i]);
+        if (d < bestd) {
+            bestd = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
 static int clampi(int v, int lo, int hi)
 {
     return v < lo ? lo : (v > hi ? hi : v);
@@ -128,7 +158,7 @@ static int clampi(int v, int lo, int hi)
 
 static int valid_shape(int fmt, int g, int64_t N, int64_t K)
 {
-    if (fmt < ORC_NF4 || fmt > ORC_NF4_DQ)
+    if (fmt < ORC_NF4 || fmt > ORC_FP4)
         return 0;
     if (g != 32 && g != 64 && g != 128)
         return 0;
@@ -157,9 +187,10 @@ static void quantize_group(int fmt, int g, const uint16_t *wg, int64_t gi,
                            int64_t e0, uint8_t *codes, void *scales,
                            uint8_t *zeros)
 {
-    if (fmt == ORC_NF4 || fmt == ORC_NF4_DQ) {
+    if (fmt == ORC_NF4 || fmt == ORC_NF4_DQ || fmt == ORC_FP4) {
         /* [hf4]: c = max|w| over the block, stored as binary32 (an fp16 value
-         * widened, so exact); code = nearest Q[i] to w / c. */
+         * widened, so exact); code = nearest Q[i] to w / c (FP4: the same
+         * with its own table; a zero block codes to its zero entry). */
         float c = 0.0f;
         for (int k = 0; k < g; ++k) {
             float a = fabsf(orc_f16_to_f32(wg[k]));
@@ -168,10 +199,10 @@ static void quantize_group(int fmt, int g, const uint16_t *wg, int64_t gi,
         }
         ((float *)scales)[gi] = c;
         for (int k = 0; k < g; ++k) {
-            int code = 7;                             /* Q[7] = 0 for c == 0 */
+            int code = fmt == ORC_FP4 ? 0 : 7;       /* the 0 entry for c == 0 */
             if (c != 0.0f) {
                 float x = orc_f16_to_f32(wg[k]) / c;  /* binary32 division */
-                code = orc_nf4_nearest(x);
+                code = fmt == ORC_FP4 ? orc_fp4_nearest(x) : orc_nf4_nearest(x);
             }
             put_nibble(codes, e0 + k, code);
         }
@@ -305,6 +336,8 @@ static float dequant_value(int fmt, int nib, int64_t gi, int64_t n_groups,
 {
     if (fmt == ORC_NF4)
         return orc_nf4_table[nib] * ((const float *)scales)[gi];
+    if (fmt == ORC_FP4)
+        return orc_fp4_table[nib] * ((const float *)scales)[gi];
     if (fmt == ORC_NF4_DQ) {
         const uint8_t *qc = (const uint8_t *)scales;
         float s2;

@@ -50,7 +50,7 @@ extern "C" {
 
 /* Format and dtype ids (the same numbering as the product ABI, defined here
  * independently). */
-enum { ORC_NF4 = 0, ORC_INT4_SYM = 1, ORC_INT4_ASYM = 2, ORC_NF4_DQ = 3 };
+enum { ORC_NF4 = 0, ORC_INT4_SYM = 1, ORC_INT4_ASYM = 2, ORC_NF4_DQ = 3, ORC_FP4 = 4 };
 
 /* Double quantization ([dq]): absmax values per second-level block. */
 enum { ORC_DQ_BLOCK = 256 };
@@ -72,8 +72,16 @@ void orc_f32_to_f16_array(const float *in, uint16_t *out, int64_t n);
 void orc_f16_to_f32_array(const uint16_t *in, float *out, int64_t n);
 void orc_f32_to_bf16_array(const float *in, uint16_t *out, int64_t n);
 
+/* The FP4 codebook (a reading, PARITY UNPINNED against the pages: [hf4]
+ * "Developer" names the fp4 quant type without a table): the E2M1 values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign bit (bit 3), divided by 6, each the
+ * nearest binary32; code = sign * 8 + 2 * e + m. */
+extern const float orc_fp4_table[16];
+
 /* Nearest NF4 index of a binary32 value x (ties to the lower index). */
 int orc_nf4_nearest(float x);
+/* Nearest FP4 index (ties to the lower index, so 0 codes as +0). */
+int orc_fp4_nearest(float x);
 void orc_nf4_nearest_array(const float *in, uint8_t *out, int64_t n);
 
 /* Second-level quantization of n absmax values c[] ([dq]): per run of
@@ -88,7 +96,7 @@ int64_t orc_dq_s2_offset(int64_t n_groups);
 /* Quantize a row-major fp16 weight W[N][K] (bit patterns) with groups of g
  * contiguous elements along K.
  *   codes  : uint8[N*K/2], byte t = nib[2t] | nib[2t+1] << 4 (flat order)
- *   scales : NF4 -> float[N*K/g] (absmax), INT4 -> uint16 fp16 bits [N*K/g],
+ *   scales : NF4, FP4 -> float[N*K/g] (absmax), INT4 -> uint16 fp16 bits [N*K/g],
  *            NF4_DQ -> bytes: uint8 qc[N*K/g] (zero-filled up to the next
  *            multiple of 16), then float s2[ceil(N*K/g / 256)]; the codes are
  *            those NF4 gives
