@@ -27,6 +27,9 @@ constexpr int kUnroll = 4;
 __constant__ float c_nf4[16] = {kNF4[0],  kNF4[1],  kNF4[2],  kNF4[3],  kNF4[4],  kNF4[5],
                                 kNF4[6],  kNF4[7],  kNF4[8],  kNF4[9],  kNF4[10], kNF4[11],
                                 kNF4[12], kNF4[13], kNF4[14], kNF4[15]};
+__constant__ float c_fp4[16] = {kFP4[0],  kFP4[1],  kFP4[2],  kFP4[3],  kFP4[4],  kFP4[5],
+                                kFP4[6],  kFP4[7],  kFP4[8],  kFP4[9],  kFP4[10], kFP4[11],
+                                kFP4[12], kFP4[13], kFP4[14], kFP4[15]};
 
 template <int OUT>
 __device__ __forceinline__ uint32_t pack2(float a, float b)
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__re
     __shared__ float tbl[16];
     if constexpr (LF == Q4_NF4) {
         if (threadIdx.x < 16)
-            tbl[threadIdx.x] = c_nf4[threadIdx.x];
+            tbl[threadIdx.x] = FMT == Q4_FP4 ? c_fp4[threadIdx.x] : c_nf4[threadIdx.x];
         __syncthreads();
     }
     const int lane = threadIdx.x & 63;
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint32_t *__re
             zp[u] = 0;
             if (unit < n_units) {
                 cw[u] = codes[unit];
-                if constexpr (FMT == Q4_NF4)
+                if constexpr (f32_absmax(FMT))
                     sc[u] = ((const float *)scales)[gi];
                 else if constexpr (FMT == Q4_NF4_DQ)  // c' = qc * s2, one product
                     sc[u] = keep_f32((float)((const uint8_t *)scales)[gi] * s2[gi / kDqRun]);
@@ -148,6 +151,8 @@ hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const voi
     switch (f) {
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(gshift, codes, scales, zeros, N, K, out_t, out, s);
+    case Q4_FP4:
+        return launch_fmt<Q4_FP4>(gshift, codes, scales, zeros, N, K, out_t, out, s);
     case Q4_NF4_DQ:
         return launch_fmt<Q4_NF4_DQ>(gshift, codes, scales, zeros, N, K, out_t, out, s);
     case Q4_INT4_SYM:

@@ -103,7 +103,7 @@ template <int FMT, int G>
 struct Span {
     static constexpr int ng = kSpanK / G;                  // groups per span (8, 4, 2)
     // bytes per scale (double-quantized NF4: the 8-bit absmax code)
-    static constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    static constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     // scale dwords per span (1 .. 8)
     static constexpr int sdw = FMT == Q4_NF4_DQ ? (ng == 8 ? 2 : 1) : ng * ss / 4;
     // loads per fragment and span: scales (16 bytes each at most), then the
@@ -210,7 +210,7 @@ template <int FMT, int G>
 __device__ __forceinline__ void wscale(const MSpan<FMT, G> &ms, int j, int sp, const TileCtx &c,
                                        int k0, float &s, float &b)
 {
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (f32_absmax(FMT)) {
         if constexpr (G == 32)
             s = std::bit_cast<float>(c.fq >= 2 ? ms.s[j][2 * sp + 1] : ms.s[j][2 * sp]);
         else
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(const uint16_t *__restrict
 
     if constexpr (level_fmt(FMT) == Q4_NF4) {
         if (t < 256)
-            ptbl[t] = float2{kNF4[t & 15], kNF4[t >> 4]};
+            ptbl[t] = float2{level_entry<FMT>(t & 15), level_entry<FMT>(t >> 4)};
     }
 
     TileCtx c;
@@ -549,6 +549,8 @@ hipError_t launch_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_
     switch (f) {
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
+    case Q4_FP4:
+        return launch_fmt<Q4_FP4>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
     case Q4_NF4_DQ:
         return launch_fmt<Q4_NF4_DQ>(g, act_t, x, M, codes, scales, zeros, N, K, y, s);
     case Q4_INT4_SYM:

@@ -121,7 +121,7 @@ __device__ __forceinline__ void dx_load(DxLoads &ld, const DxCtx &c, int n0_, in
     const int k = k0 + 16 * (t & 7);
     ld.c = __builtin_amdgcn_raw_buffer_load_b64(c.cr, n * (c.K >> 1) + (k >> 1), 0, 0);
     const int gi = n * c.G + (k >> c.gshift);  // flat group index of the 16 columns
-    if constexpr (FMT == Q4_NF4) {
+    if constexpr (f32_absmax(FMT)) {
         ld.s = __builtin_amdgcn_raw_buffer_load_b32(c.sr, 4 * gi, 0, 0);
     } else if constexpr (FMT == Q4_NF4_DQ) {
         ld.s = __builtin_amdgcn_raw_buffer_load_b8(c.sr, gi, 0, 0);
@@ -161,11 +161,11 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
     const int fi = lane & 15, fq = lane >> 4;
     const int m0 = (int)(blockIdx.x % (unsigned)mtiles) * TM;
     const int k0 = (int)(blockIdx.x / (unsigned)mtiles) * TK;
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
 
     if constexpr (level_fmt(FMT) == Q4_NF4) {
         if (t < 256)
-            ptbl[t] = float2{kNF4[t & 15], kNF4[t >> 4]};
+            ptbl[t] = float2{level_entry<FMT>(t & 15), level_entry<FMT>(t >> 4)};
     }
 
     DxCtx c;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
         u32x4 wv[2];
         auto dequant = [&](int e) {
             float sc, bias = 0.0f;
-            if constexpr (FMT == Q4_NF4) {
+            if constexpr (f32_absmax(FMT)) {
                 sc = std::bit_cast<float>(ld.s);
             } else if constexpr (FMT == Q4_NF4_DQ) {
                 sc = keep_f32((float)(ld.s & 0xffu) * std::bit_cast<float>(ld.z));
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kBlock) void gemm_dx_kernel(const uint16_t *__restr
             *(u32x4 *)(ys[0] + yr * kYRow + 16 * yswz(yr, t & 7)) = la.y[i];
         }
         float sc, bias = 0.0f;
-        if constexpr (FMT == Q4_NF4) {
+        if constexpr (f32_absmax(FMT)) {
             sc = std::bit_cast<float>(la.s);
         } else if constexpr (FMT == Q4_NF4_DQ) {
             sc = keep_f32((float)(la.s & 0xffu) * std::bit_cast<float>(la.z));
@@ -383,6 +383,8 @@ hipError_t launch_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, in
     switch (f) {
     case Q4_NF4:
         return launch_dx_fmt<Q4_NF4>(act_t, gshift, dy, M, codes, scales, zeros, N, K, dx, s);
+    case Q4_FP4:
+        return launch_dx_fmt<Q4_FP4>(act_t, gshift, dy, M, codes, scales, zeros, N, K, dx, s);
     case Q4_NF4_DQ:
         return launch_dx_fmt<Q4_NF4_DQ>(act_t, gshift, dy, M, codes, scales, zeros, N, K, dx, s);
     case Q4_INT4_SYM:

@@ -94,10 +94,10 @@ template <int FMT>
 __device__ __forceinline__ float nf4_lane_entry()
 {
     const int i = threadIdx.x & 15;
-    float v = kNF4[0];
+    float v = level_entry<FMT>(0);
 #pragma unroll
     for (int k = 1; k < 16; ++k)
-        v = i == k ? kNF4[k] : v;
+        v = i == k ? level_entry<FMT>(k) : v;
     return v;
 }
 template <int FMT>
@@ -194,7 +194,7 @@ __device__ __forceinline__ RowRef row_ref(const uint8_t *codes, const void *scal
                                           const uint8_t *zeros, int64_t n0, int64_t N,
                                           int64_t row_bytes, int64_t G)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     RowRef r;
     r.live = n0 < N;
     r.codes = codes + n0 * row_bytes;
@@ -239,7 +239,7 @@ struct LaneOffs {
 template <int FMT>
 __device__ __forceinline__ LaneOffs lane_offs(int lane, int gshift)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     LaneOffs o;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -273,7 +273,7 @@ template <int FMT>
 __device__ __forceinline__ void load_stage(Stage &st, const RowRef &r, int s, const LaneOffs &lo,
                                            int row_bytes, int G, int gshift)
 {
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
     const int cs = 16 * kStageChunks * s;                 // the stage's first code byte
     const int gs = (kStageChunks * 32 * s) >> gshift;      // the stage's first group in the row
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(r.codes + cs, r.live ? row_bytes - cs : 0);
@@ -281,7 +281,7 @@ __device__ __forceinline__ void load_stage(Stage &st, const RowRef &r, int s, co
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         st.cw[h] = __builtin_amdgcn_raw_buffer_load_b128(cr, lo.cd[h], 0, kNT);
-        if constexpr (FMT == Q4_NF4)
+        if constexpr (f32_absmax(FMT))
             st.sc[h] = std::bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(sr, lo.sc[h], 0, kNT));
         else if constexpr (FMT == Q4_NF4_DQ)  // the 8-bit code; the constant below
             st.sc[h] = std::bit_cast<float>((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, lo.sc[h], 0, kNT));
@@ -1307,6 +1307,8 @@ hipError_t launch_gemv_chain(q4_format f, int g, q4_dtype act_t, const q4_gemv_t
     switch (f) {
     case Q4_NF4:
         return bf ? launch_chain_t<Q4_NF4, Q4_BF16>(a, s) : launch_chain_t<Q4_NF4, Q4_F16>(a, s);
+    case Q4_FP4:
+        return bf ? launch_chain_t<Q4_FP4, Q4_BF16>(a, s) : launch_chain_t<Q4_FP4, Q4_F16>(a, s);
     case Q4_NF4_DQ:
         return bf ? launch_chain_t<Q4_NF4_DQ, Q4_BF16>(a, s)
                   : launch_chain_t<Q4_NF4_DQ, Q4_F16>(a, s);
@@ -1330,6 +1332,8 @@ hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_
     switch (f) {
     case Q4_NF4:
         return launch_act<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    case Q4_FP4:
+        return launch_act<Q4_FP4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_NF4_DQ:
         return launch_act<Q4_NF4_DQ>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_INT4_SYM:

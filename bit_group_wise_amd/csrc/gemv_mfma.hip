@@ -81,11 +81,11 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const int n0 = blockIdx.x * 16 * RB;
     const int G = K >> gshift;
     const int row_bytes = K >> 1;
-    constexpr int ss = FMT == Q4_NF4 ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
+    constexpr int ss = f32_absmax(FMT) ? 4 : (FMT == Q4_NF4_DQ ? 1 : 2);
 
     if constexpr (LF == Q4_NF4) {
         if (threadIdx.x < 256)
-            ptbl[threadIdx.x] = float2{kNF4[threadIdx.x & 15], kNF4[threadIdx.x >> 4]};
+            ptbl[threadIdx.x] = float2{level_entry<FMT>(threadIdx.x & 15), level_entry<FMT>(threadIdx.x >> 4)};
     }
 
     // views: this workgroup's 16 RB weight rows (rows past N read zeros) and
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
             st.cw[b] = __builtin_amdgcn_raw_buffer_load_b128(cr, in ? rr * row_bytes + (k >> 1) : -16,
                                                              0, 0);
             const int gi = rr * G + (k >> gshift);  // group within the workgroup's rows
-            if constexpr (FMT == Q4_NF4)
+            if constexpr (f32_absmax(FMT))
                 st.sraw[b] = __builtin_amdgcn_raw_buffer_load_b32(sr, in ? 4 * gi : -16, 0, 0);
             else if constexpr (FMT == Q4_NF4_DQ)
                 st.sraw[b] = __builtin_amdgcn_raw_buffer_load_b8(sr, in ? gi : -16, 0, 0);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
                 if (step + kSkWaves * i >= nsteps)
                     break;
                 float s, bias;
-                if constexpr (FMT == Q4_NF4) {
+                if constexpr (f32_absmax(FMT)) {
                     s = std::bit_cast<float>(st.sraw[b]);
                     bias = 0.0f;
                 } else if constexpr (FMT == Q4_NF4_DQ) {  // c' = qc * s2, one product
@@ -269,6 +269,8 @@ hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, i
     switch (f) {
     case Q4_NF4:
         return launch_sk_fmt<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    case Q4_FP4:
+        return launch_sk_fmt<Q4_FP4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_NF4_DQ:
         return launch_sk_fmt<Q4_NF4_DQ>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
     case Q4_INT4_SYM:

@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "q4.h"
+#include "q4_common.hpp"
 #include "q4_internal.hpp"
 
 // The sync words of q4_gemv_chain_static: one chain's finished-workgroup
@@ -48,7 +49,7 @@ hipError_t scratch_for_current_device(uint32_t **out)
 
 bool format_ok(q4_format f)
 {
-    return f == Q4_NF4 || f == Q4_INT4_SYM || f == Q4_INT4_ASYM || f == Q4_NF4_DQ;
+    return f == Q4_NF4 || f == Q4_INT4_SYM || f == Q4_INT4_ASYM || f == Q4_NF4_DQ || f == Q4_FP4;
 }
 bool dtype_ok(q4_dtype t) { return t == Q4_F16 || t == Q4_BF16; }
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
@@ -66,7 +67,7 @@ q4_status check_weight(q4_format f, int g, const void *codes, const void *scales
         return Q4_EINVAL;
     if ((f == Q4_INT4_ASYM) != (zeros != nullptr))
         return Q4_EINVAL;
-    const uintptr_t sa = f == Q4_NF4_DQ ? 16 : (f == Q4_NF4 ? 4 : 2);
+    const uintptr_t sa = f == Q4_NF4_DQ ? 16 : (q4::f32_absmax(f) ? 4 : 2);
     if (!aligned(codes, 16) || !aligned(scales, sa))
         return Q4_EALIGN;
     return Q4_OK;
@@ -95,7 +96,7 @@ size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g)
         return 0;
     if (f == Q4_NF4_DQ)
         return pad16(q4::dq_scales_bytes(N * (K / g)));
-    return pad16(N * (K / g) * (f == Q4_NF4 ? 4 : 2));
+    return pad16(N * (K / g) * (q4::f32_absmax(f) ? 4 : 2));
 }
 
 size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g)

@@ -31,9 +31,35 @@ inline constexpr float kNF4[16] = {-1.0f,  -0.696f, -0.525f, -0.395f, -0.284f, -
                                    -0.091f, 0.0f,   0.079f,  0.161f,  0.246f,  0.338f,
                                    0.441f,  0.562f, 0.720f,  1.0f};
 
-// NF4 with double-quantized absmax decodes as NF4 once each block's absmax
-// has been recovered: the level arithmetic of a format.
-constexpr int level_fmt(int f) { return f == Q4_NF4_DQ ? Q4_NF4 : f; }
+// FP4 ("Loading a model in 4-bit", "Developer", names the fp4 quant type
+// beside nf4 without printing its table; a reading): the E2M1 element values
+// -- bit 3 the sign, bits 2..1 an exponent e, bit 0 a mantissa bit m; m / 2
+// for e = 0, else 2^(e-1) (1 + m / 2) -- divided by 6 so that the largest
+// magnitude is 1, each the nearest binary32 of the exact fraction, used as
+// NF4's table is (scaled by the binary32 block absmax).  Code 8 is -0.
+constexpr float e2m1_over_6(int c)
+{
+    const int e = (c >> 1) & 3, m = c & 1;
+    const double mag = e == 0 ? 0.5 * m : (double)(1 << (e - 1)) * (1.0 + 0.5 * m);
+    const float v = (float)(mag / 6.0);
+    return (c & 8) ? -v : v;
+}
+inline constexpr float kFP4[16] = {
+    e2m1_over_6(0),  e2m1_over_6(1),  e2m1_over_6(2),  e2m1_over_6(3),
+    e2m1_over_6(4),  e2m1_over_6(5),  e2m1_over_6(6),  e2m1_over_6(7),
+    e2m1_over_6(8),  e2m1_over_6(9),  e2m1_over_6(10), e2m1_over_6(11),
+    e2m1_over_6(12), e2m1_over_6(13), e2m1_over_6(14), e2m1_over_6(15)};
+static_assert(kFP4[7] == 1.0f && kFP4[15] == -1.0f && kFP4[5] == 0.5f, "E2M1 / 6");
+
+// The level arithmetic of a format: NF4 with double-quantized absmax decodes
+// as NF4 once each block's absmax has been recovered, and FP4 as NF4 with its
+// own table (16 binary32 levels times the block absmax).
+constexpr int level_fmt(int f) { return (f == Q4_NF4_DQ || f == Q4_FP4) ? Q4_NF4 : f; }
+// Formats whose stored scale is the binary32 block absmax itself.
+constexpr bool f32_absmax(int f) { return f == Q4_NF4 || f == Q4_FP4; }
+// Level i of a table format's codebook.
+template <int FMT>
+constexpr float level_entry(int i) { return FMT == Q4_FP4 ? kFP4[i] : kNF4[i]; }
 
 // Compile-time IEEE helpers (finite inputs only).
 constexpr uint32_t f32_bits(float f) { return std::bit_cast<uint32_t>(f); }
@@ -114,6 +140,23 @@ constexpr float nf4_threshold(int i)
         f = next_up(f);
     return f;
 }
+
+// FP4 coding by the magnitude: the nearest entry to x (ties to the lower
+// index) is +-level j, with j the number of thresholds u_j <= |x| (u_j the
+// smallest binary32 strictly above the exact midpoint of magnitudes j and
+// j + 1, codes 0..7 ascending), and code j + 8 for x < 0 unless j = 0 (the
+// tie between +0 and -0 keeps code 0).
+constexpr float fp4_threshold(int j)
+{
+    double m = ((double)kFP4[j] + (double)kFP4[j + 1]) * 0.5;
+    float f = (float)m;
+    if ((double)f <= m)
+        f = next_up(f);
+    return f;
+}
+inline constexpr float kFP4Thr[7] = {fp4_threshold(0), fp4_threshold(1), fp4_threshold(2),
+                                     fp4_threshold(3), fp4_threshold(4), fp4_threshold(5),
+                                     fp4_threshold(6)};
 
 // Bucket table: x in [-1, 1] falls into bucket b = floor((x + 1) * 16) (b in
 // 0..32).  The bucket width 1/16 is below the smallest gap between

@@ -17,7 +17,8 @@
 // e = fma(-q0, s, w); q = fma(e, r, q0)), which equals the correctly rounded
 // IEEE quotient for every pair of fp16 operands with s > 0 (checked
 // exhaustively on all such pairs); NF4 codes come from a 33-bucket table of
-// exact decision thresholds held in LDS.
+// exact decision thresholds held in LDS, FP4 codes from seven exact
+// thresholds on the magnitude and the sign.
 //
 // NF4 with double-quantized absmax (the same page, "Where the accuracy
 // goes", and its closing section on NF4: the block constants coded again in
@@ -83,6 +84,27 @@ __device__ __forceinline__ uint32_t nf4_word(const float (&v)[8], float c, const
     return word;
 }
 
+// FP4 codes of 8 weights of a group with absmax c > 0: the magnitude index
+// j = number of thresholds at or below |x| (seven compares), then the sign
+// (code j + 8 for x < 0 and j > 0; the tie of +0 and -0 keeps code 0).
+__device__ __forceinline__ uint32_t fp4_word(const float (&v)[8], float c)
+{
+    const float r = 1.0f / c;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = div_mk(v[i], c, r);
+        const float a = fabsf(x);
+        uint32_t j = 0;
+#pragma unroll
+        for (int t = 0; t < 7; ++t)
+            j += a >= kFP4Thr[t] ? 1u : 0u;
+        const uint32_t code = (x < 0.0f && j != 0) ? j + 8 : j;
+        word |= code << (4 * i);
+    }
+    return word;
+}
+
 template <int FMT, int G>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restrict__ w,
                                                           uint32_t *__restrict__ codes,
@@ -122,13 +144,16 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
             uint32_t word = 0;
             const int64_t gi = slot / LPG;
             const bool leader = (lane % LPG) == 0;
-            if constexpr (FMT == Q4_NF4) {
+            if constexpr (FMT == Q4_NF4 || FMT == Q4_FP4) {
                 float a = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     a = fmaxf(a, fabsf(v[i]));
                 const float c = group_max<LPG>(a);
-                word = c != 0.0f ? nf4_word(v, c, lut) : 0x77777777u;
+                if constexpr (FMT == Q4_NF4)
+                    word = c != 0.0f ? nf4_word(v, c, lut) : 0x77777777u;
+                else
+                    word = c != 0.0f ? fp4_word(v, c) : 0u;
                 if (in && leader)
                     ((float *)scales)[gi] = c;
             } else if constexpr (FMT == Q4_INT4_SYM) {
@@ -338,6 +363,8 @@ hipError_t launch_quantize(q4_format f, int g, const void *w, int64_t N, int64_t
                                   : launch_dq<128>(w, N, K, codes, scales, s));
     case Q4_NF4:
         return launch_fmt<Q4_NF4>(g, w, N, K, codes, scales, zeros, s);
+    case Q4_FP4:
+        return launch_fmt<Q4_FP4>(g, w, N, K, codes, scales, zeros, s);
     case Q4_INT4_SYM:
         return launch_fmt<Q4_INT4_SYM>(g, w, N, K, codes, scales, zeros, s);
     default:

@@ -12,10 +12,10 @@ import ctypes
 import os
 import threading
 
-NF4, INT4_SYM, INT4_ASYM, NF4_DQ = 0, 1, 2, 3
+NF4, INT4_SYM, INT4_ASYM, NF4_DQ, FP4 = 0, 1, 2, 3, 4
 DQ_RUN = 256  # absmax values per second-level constant (NF4_DQ)
 F16, BF16 = 0, 1
-FORMATS = {"nf4": NF4, "int4_sym": INT4_SYM, "int4_asym": INT4_ASYM, "nf4_dq": NF4_DQ}
+FORMATS = {"nf4": NF4, "int4_sym": INT4_SYM, "int4_asym": INT4_ASYM, "nf4_dq": NF4_DQ, "fp4": FP4}
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, 1, 2, 3, 4
 
@@ -147,10 +147,10 @@ def alloc_quantized(fmt: int, g: int, N: int, K: int, device) -> QuantizedWeight
         # uint8 qc[N*G], zero bytes to a multiple of 16, float32 s2[runs]
         scales = torch.zeros((ns,), dtype=torch.uint8, device=device)[: dq_scales_size(N * (K // g))]
         return QuantizedWeight(fmt, g, N, K, codes, scales, zeros)
-    sdt = torch.float32 if fmt == NF4 else torch.float16
+    sdt = torch.float32 if fmt in (NF4, FP4) else torch.float16
     # scale and zero-point storage carries the ABI's padding to 16 bytes;
     # the tensors handed out are views of the meaningful leading part
-    es = 4 if fmt == NF4 else 2
+    es = 4 if fmt in (NF4, FP4) else 2
     scales = torch.zeros((ns // es,), dtype=sdt, device=device)[: N * (K // g)].view(N, K // g)
     return QuantizedWeight(fmt, g, N, K, codes, scales, zeros)
 

@@ -32,12 +32,19 @@
  *     to about 0.127 bits per parameter).  The 8-bit coding is not spelled
  *     out; it is read here as symmetric absmax int8 with a binary32 constant
  *     per run of 256 absmax values (rules below).
+ *   - FP4 (Q4_FP4): "Loading a model in 4-bit", "Developer", names the fp4
+ *     quant type beside nf4 without printing its codebook.  Read here as the
+ *     E2M1 element values (bit 3 the sign, bits 2..1 an exponent e, bit 0 a
+ *     mantissa bit m: m/2 for e = 0, else 2^(e-1) (1 + m/2), i.e. 0, 0.5, 1,
+ *     1.5, 2, 3, 4, 6) divided by 6, each the nearest binary32, used exactly
+ *     as NF4's table (block absmax, nearest entry).  Its agreement with any
+ *     other fp4 implementation is not established by the pages.
  *
  * Data layout (all row-major, W is [N, K] like a Linear layer's weight):
  *   w       fp16 [N, K]
  *   codes   uint8 [N, K/2]; byte t of the flat array holds element 2t in its
  *           low nibble and element 2t+1 in its high nibble.
- *   scales  NF4: float32 [N, K/g] (the block absmax c)
+ *   scales  NF4, FP4: float32 [N, K/g] (the block absmax c)
  *           INT4-sym / INT4-asym: fp16 [N, K/g]
  *           NF4_DQ: bytes.  uint8 qc[N*K/g] (the 8-bit absmax codes in flat
  *           group order r*(K/g) + j), zero bytes up to the next multiple of
@@ -58,10 +65,12 @@
  *   ASYM  lo = min(0, min w), hi = max(0, max w); s = fp16((hi - lo) / 15);
  *         z = clamp(rint(-lo / s), 0, 15); nibble = clamp(rint(w / s) + z,
  *         0, 15); s == 0 gives z = 0 and nibble 0.
+ *   FP4   as NF4 with the FP4 table; ties to the lower index, so 0 codes as
+ *         +0 (code 0); c == 0 gives code 0.
  *   NF4_DQ codes exactly as NF4 (with the exact absmax c); then per run of
  *         256 absmax values, s2 = c2 / 127 with c2 the run's max, and
  *         qc = clamp(rint(c / s2), 0, 127) (0 where s2 == 0).
- * Dequantize: NF4 Q[i] * c, SYM (nibble - 8) * s, ASYM (nibble - z) * s, one
+ * Dequantize: NF4 and FP4 Q[i] * c, SYM (nibble - 8) * s, ASYM (nibble - z) * s, one
  * binary32 product rounded once (nearest-even) to fp16 or bf16.  NF4_DQ first
  * recovers c' = qc * s2 (one binary32 product), then Q[i] * c' as NF4.
  *
@@ -76,7 +85,7 @@
  *     crosses the ABI.  Faults inside a kernel surface at the caller's next
  *     synchronisation.
  *   - Alignment: w, codes, x and out must be 16-byte aligned (the kernels
- *     move 16 bytes per lane); scales must be 4-byte (NF4), 2-byte (INT4) or
+ *     move 16 bytes per lane); scales must be 4-byte (NF4, FP4), 2-byte (INT4) or
  *     16-byte (NF4_DQ) aligned, y 2-byte aligned.  There is no slow fallback path.
  *   - Preconditions not checked: inputs are finite; output buffers do not
  *     alias inputs; the buffers are at least the sizes q4_*_bytes report.
@@ -91,7 +100,7 @@
 extern "C" {
 #endif
 
-typedef enum { Q4_NF4 = 0, Q4_INT4_SYM = 1, Q4_INT4_ASYM = 2, Q4_NF4_DQ = 3 } q4_format;
+typedef enum { Q4_NF4 = 0, Q4_INT4_SYM = 1, Q4_INT4_ASYM = 2, Q4_NF4_DQ = 3, Q4_FP4 = 4 } q4_format;
 typedef enum { Q4_F16 = 0, Q4_BF16 = 1 } q4_dtype;
 typedef enum {
     Q4_OK = 0,
@@ -107,7 +116,7 @@ typedef enum {
 /* Sizes in bytes of the caller-allocated buffers for an [N, K] weight with
  * groups of g (0 for invalid arguments).
  *   codes:  exactly N*K/2.
- *   scales: the meaningful size -- N*(K/g)*4 (NF4), N*(K/g)*2 (INT4), or
+ *   scales: the meaningful size -- N*(K/g)*4 (NF4, FP4), N*(K/g)*2 (INT4), or
  *           for NF4_DQ the 8-bit codes padded to a multiple of 16 plus
  *           4*ceil(N*(K/g)/256) -- plus P bytes of trailing padding;
  *   zeros:  the meaningful size ceil(N*(K/g)/2) (INT4-asym; 0 otherwise)
@@ -121,7 +130,7 @@ typedef enum {
  * allocate the padded size (the padding's contents are never used and may
  * be anything).  q4_quantize writes only the meaningful bytes. */
 size_t q4_codes_bytes(int64_t N, int64_t K);                      /* N*K/2 */
-size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4, 2 INT4), padded;
+size_t q4_scales_bytes(q4_format f, int64_t N, int64_t K, int g); /* N*K/g * (4 NF4/FP4, 2 INT4), padded;
                                                                       NF4_DQ: qc, s2 as above, padded */
 size_t q4_zeros_bytes(q4_format f, int64_t N, int64_t K, int g);  /* asym: ceil(N*K/g / 2), padded; else 0 */
 

@@ -24,7 +24,7 @@ def gpu_quantize(fmt, g, w_bits):
     q = q4.quantize(dev16(w_bits), fmt, g)
     torch.cuda.synchronize()
     codes = q.codes.cpu().numpy()
-    if fmt in (q4.NF4, q4.NF4_DQ):   # float32 [N, G], or the NF4_DQ byte buffer
+    if fmt in (q4.NF4, q4.NF4_DQ, q4.FP4):   # float32 [N, G], or the NF4_DQ byte buffer
         scales = q.scales.cpu().numpy()
     else:
         scales = q.scales.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -38,7 +38,7 @@ def assert_quant_equal(fmt, g, w_bits, tag=""):
     oc, os_, oz = oracle.quantize(fmt, g, w_bits)
     bad = np.argwhere(codes != oc)
     assert bad.size == 0, f"{tag} codes differ at {bad[:5].tolist()} gpu={codes[tuple(bad[0])]:#x} orc={oc[tuple(bad[0])]:#x}"
-    if fmt == q4.NF4:
+    if fmt in (q4.NF4, q4.FP4):
         assert np.array_equal(scales.view(np.uint32), os_.view(np.uint32)), f"{tag} scales differ"
     elif fmt == q4.NF4_DQ:
         # 8-bit absmax codes, the zero gap and the binary32 constants

@@ -84,6 +84,9 @@ def test_size_helpers_invalid():
     assert q4.zeros_bytes(q4.INT4_ASYM, 3, 96, 32) == 32
     assert q4.scales_bytes(q4.INT4_SYM, 3, 96, 32) == 48
     assert q4.scales_bytes(q4.NF4, 1, 128, 64) == 32
+    # FP4: binary32 absmax like NF4, no zero-points
+    assert q4.scales_bytes(q4.FP4, 1, 128, 64) == 32
+    assert q4.zeros_bytes(q4.FP4, 4, 128, 64) == 0
     # NF4_DQ: 9 codes padded to 16, one 4-byte constant, then the padding
     assert q4.scales_bytes(q4.NF4_DQ, 3, 96, 32) == 48
     # 1024 groups: 1024 code bytes + 4 constants (0.127 bits per weight) + 16
@@ -107,7 +110,7 @@ def call_gemv(fmt=q4.NF4, g=64, act=q4.BF16, x=A, M=1, codes=A, scales=A, zeros=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=4), q4.EUNSUPPORTED),
+    (dict(fmt=5), q4.EUNSUPPORTED),
     (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),   # NF4_DQ scales need 16 bytes
     (dict(fmt=q4.NF4_DQ, zeros=A), q4.EINVAL),
     (dict(g=16), q4.EUNSUPPORTED),
@@ -123,6 +126,8 @@ def call_gemv(fmt=q4.NF4, g=64, act=q4.BF16, x=A, M=1, codes=A, scales=A, zeros=
     (dict(w=MIS), q4.EALIGN),
     (dict(codes=MIS), q4.EALIGN),
     (dict(scales=MIS), q4.EALIGN),                 # NF4 scales need 4 bytes
+    (dict(fmt=q4.FP4, scales=MIS), q4.EALIGN),     # FP4 scales need 4 bytes
+    (dict(fmt=q4.FP4, zeros=A), q4.EINVAL),        # zeros for FP4
 ])
 def test_quantize_rejects(kw, status):
     assert call_quantize(**kw) == status
@@ -192,7 +197,7 @@ def test_gemv_task_layout():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=4), q4.EUNSUPPORTED),
+    (dict(fmt=5), q4.EUNSUPPORTED),
     (dict(fmt=q4.NF4_DQ, scales=0x10004), q4.EALIGN),   # NF4_DQ scales need 16 bytes
     (dict(fmt=q4.NF4_DQ, zeros=A), q4.EINVAL),
     (dict(g=16), q4.EUNSUPPORTED),

@@ -23,7 +23,7 @@ from _helpers import DEV, TORCH_ACT, assert_product_ok, dev16
 pytestmark = pytest.mark.gpu
 
 GROUPS = {q4.NF4: [32, 64, 128], q4.INT4_SYM: [32, 64, 128], q4.INT4_ASYM: [32, 64, 128],
-          q4.NF4_DQ: [32, 64, 128]}
+          q4.NF4_DQ: [32, 64, 128], q4.FP4: [32, 64, 128]}
 
 
 def _weight(N, K, fmt, g, seed, sigma=0.02):
@@ -75,7 +75,7 @@ def _assert_same(outs, ref, tag):
 
 
 @pytest.mark.parametrize("act", [q4.BF16, q4.F16])
-@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ])
+@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4])
 def test_chain_equals_consecutive_gemv(fmt, act):
     for g in GROUPS[fmt]:
         tag = f"fmt{fmt} g{g} act{act}"

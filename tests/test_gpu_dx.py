@@ -23,7 +23,7 @@ SHAPES = [(256, 64, 128), (37, 200, 288), (300, 136, 1024), (513, 1032, 160), (1
 
 
 @pytest.mark.parametrize("act", [q4.BF16, q4.F16])
-@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ])
+@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4])
 def test_dx_against_oracle(fmt, act):
     for g in (32, 64, 128):
         for M, N, K in SHAPES:

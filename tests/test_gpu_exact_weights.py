@@ -32,7 +32,7 @@ from _helpers import DEV, TORCH_ACT, assert_product_ok, dev16, host16
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ]
+FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4]
 
 F16_ONE_PLUS = {1: 0x3C04, 3: 0x3C0C}  # fp16 1 + 2^-8 and 1 + 3 * 2^-8 (bf16 midpoints)
 
@@ -45,7 +45,8 @@ def tie_rows(fmt, g, N, K):
     """fp16 weights whose dequantized values are mostly bf16 midpoints.
 
     Group j of row r uses t = 1 + 2^-8 or 1 + 3 * 2^-8 (alternating) as the
-    level-1 value: NF4 blocks hold t everywhere (absmax t, code 15, what = t);
+    level-1 value: NF4 and FP4 blocks hold t everywhere (absmax t, the code of
+    level 1, what = t);
     INT4-sym groups hold 7t (absmax, so the scale is exactly t) and +-t
     (levels +-1); INT4-asym groups hold a maximum whose range / 15 rounds to
     the fp16 scale t, then t (level 1, zero-point 0)."""
@@ -73,9 +74,10 @@ def unrounded(fmt, g, codes, scales, zeros, N, K):
     nib[:, 0::2] = codes & 0xF
     nib[:, 1::2] = codes >> 4
     G = K // g
-    if fmt == q4.NF4:
+    if fmt in (q4.NF4, q4.FP4):
         s = scales.astype(np.float64).reshape(N, G)
-        lv = oracle.nf4_table().astype(np.float64)[nib]
+        table = oracle.fp4_table() if fmt == q4.FP4 else oracle.nf4_table()
+        lv = table.astype(np.float64)[nib]
     elif fmt == q4.NF4_DQ:
         qc, s2 = oracle.dq_split(scales, N * G)
         c = (qc.astype(np.float32) * s2[np.arange(N * G) // oracle.DQ_BLOCK]).astype(np.float32)
@@ -189,7 +191,7 @@ def test_f16_subnormal_weights(fmt):
     rng = np.random.default_rng(55)
     w = f16(rng.standard_normal((N, K)).astype(np.float32) * 1e-6)
     case, x, gapsum = adversarial_case(fmt, g, q4.F16, w, 1000.0)
-    if fmt in (q4.NF4, q4.NF4_DQ):
+    if fmt in (q4.NF4, q4.NF4_DQ, q4.FP4):
         _check_adversarial(case, x, gapsum, fmt, g, q4.F16, N, K, ratio=2.0)
     q = _weight_on_gpu(fmt, g, w, case)
     _products(fmt, g, q4.F16, q, x, case, tag=f"f16 subnormal fmt{fmt}")

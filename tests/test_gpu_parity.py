@@ -17,7 +17,7 @@ from _helpers import DEV, TORCH_ACT, assert_product_ok, assert_quant_equal, dev1
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ]
+FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4]
 GS = [32, 64, 128]
 
 
@@ -84,7 +84,7 @@ def test_quantize_exhaustive_fp16(fmt):
     w = np.concatenate(rows, 0)
     for g in GS:
         assert_quant_equal(fmt, g, w, tag=f"exhaustive fmt{fmt} g{g}")
-    if fmt == q4.NF4:
+    if fmt in (q4.NF4, q4.FP4):
         unit = vals[np.abs(vals.view(np.float16).astype(np.float32)) <= 1.0]
         n63 = (unit.size + 62) // 63
         pad = np.concatenate([unit, np.zeros(n63 * 63 - unit.size, np.uint16)])

@@ -56,7 +56,7 @@ def _setup(fmt, g, N, K, seed):
     return tailed_weight(q), oracle.quantize(fmt, g, w)
 
 
-FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ]
+FMTS = [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
