@@ -28,12 +28,14 @@ launch stream:
     the prefill shape and at M = 16 on an 11008x4096 NF4 weight, beside the
     fused kernels,
   * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
-    INT4-sym g128 4096x4096 at M = 1, NF4 g64 11008x4096 and 4096x11008 at
-    M = 1, 4, 16,
+    NF4 g64 1024x1024 and INT4-sym g128 4096x4096 at M = 1, NF4 g64
+    11008x4096 and 4096x11008 at M = 1, 4, 16,
+  * a plain 1 GiB device copy, the streaming ceiling read beside the rates,
   * quantize and dequantize of the single-matrix workloads in their own
     formats on cold buffers,
   * the CPU oracle on a time-bounded sample of the token, on one thread and
-    on the host's cores (cpu_baseline).
+    on the host's cores (cpu_baseline), and on samples of the INT4-asym
+    quantize, dequantize and GEMM reference (cpu_baseline.other_ops).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -295,6 +297,7 @@ def main():
         extra = extra_legs(torch, q4, dev, stream)
         extra["gemv_configs_cold"] = config_gemvs(torch, q4, dev, stream)
         extra["codec_configs_cold"] = codec_configs(torch, q4, dev, stream)
+        extra["hbm_copy_ceiling"] = copy_ceiling(torch, dev, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -544,11 +547,28 @@ def codec_configs(torch, q4, dev, stream):
     }
 
 
+def copy_ceiling(torch, dev, stream):
+    """A plain 1 GiB device-to-device copy (read + write), the streaming
+    ceiling beside which the kernels' GB/s are read (context, not a peak)."""
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    ms = _timer(torch, stream)(lambda: b.copy_(a), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * n, "ms": round(ms, 4),
+            "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * 2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+
+
 def config_gemvs(torch, q4, dev, stream):
-    """The single-matrix GEMV configurations on cold weights: INT4-sym g128
+    """The single-matrix GEMV configurations on cold weights: NF4 g64
+    1024x1024 (fp16 x, M = 1), INT4-sym g128
     4096x4096 (fp16 x, M = 1) and the NF4 g64 MLP shapes 11008x4096 and
     4096x11008 (bf16 x, M = 1, 4, 16)."""
     return {
+        "c1_nf4_g64_1024x1024_f16": _rotated_gemv(torch, q4, dev, stream, q4.NF4, 64,
+                                                  1024, 1024, [1], q4.F16, 102),
         "c2_sym_g128_4096x4096_f16": _rotated_gemv(torch, q4, dev, stream, q4.INT4_SYM, 128,
                                                    4096, 4096, [1], q4.F16, 203),
         "c3_nf4_g64_11008x4096_bf16": _rotated_gemv(torch, q4, dev, stream, q4.NF4, 64,
@@ -697,11 +717,13 @@ def cpu_baseline(seconds: float):
             i += 4 * T
             doneT += sum(ex.map(run, batch))
     tT = time.perf_counter() - t0
+    others = _cpu_other_ops(T, max(2.0, seconds / 8))
     return {
         "value": round(doneT / tT / 1e9, 4),
         "unit": "GB/s",
         "cores": T,
         "kind": "oracle",
+        "other_ops": others,
         "sample": f"{len(blocks)} blocks of 64 weight rows (the first 2048 rows of each of "
                   f"{blocks[0][0]} .. {blocks[-1][0]}), NF4 g64, M=1 bf16: dequantize + fp64 dot "
                   f"product, cycled for {tT:.1f}s on {T} threads ({doneT / 2**20:.0f} MiB); "
@@ -709,6 +731,47 @@ def cpu_baseline(seconds: float):
         "value_one_thread": round(done1 / t1 / 1e9, 4),
         "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_other_ops(T: int, seconds: float):
+    """The oracle on the other ops, T threads, each cycled for about
+    `seconds`: quantize and dequantize of the INT4-asym g32 prefill weight
+    (blocks of 64 of its 14336 rows; algorithmic GB/s as on the GPU) and the
+    fp64 GEMM reference on a row sample of that workload (64 rows of x
+    against 256 weight rows at a time; GFLOP/s of 2 M N K)."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    from bit_group_wise_amd import synth
+
+    K, g, rows = 4096, 32, 64
+    w = [synth.weight_f16_bits(rows, K, seed=401 + i, mu=0.001) for i in range(4 * T)]
+    q = [oracle.quantize(oracle.INT4_ASYM, g, b) for b in w]
+    nb = rows * K * 2 + rows * K // 2 + rows * (K // g) * 2 + rows * (K // g) // 2
+    x = synth.act_bits(64, K, 402, synth.BF16)
+    wq = [oracle.quantize(oracle.INT4_ASYM, g, synth.weight_f16_bits(256, K, seed=450 + i,
+                                                                      mu=0.001))
+          for i in range(T)]
+
+    def cycle(fn, items):
+        done, t0, i = 0, time.perf_counter(), 0
+        with cf.ThreadPoolExecutor(T) as ex:
+            while time.perf_counter() - t0 < seconds:
+                done += sum(ex.map(fn, [items[(i + j) % len(items)] for j in range(T)]))
+                i += T
+        return done / (time.perf_counter() - t0)
+
+    qr = cycle(lambda b: (oracle.quantize(oracle.INT4_ASYM, g, b), nb)[1], w)
+    dr = cycle(lambda c: (oracle.dequantize(oracle.INT4_ASYM, g, c[0], c[1], c[2], rows, K,
+                                            oracle.BF16), nb)[1], q)
+    fr = cycle(lambda c: (oracle.matmul(oracle.INT4_ASYM, g, oracle.BF16, x, c[0], c[1], c[2],
+                                        256, K), 2.0 * 64 * 256 * K)[1], wq)
+    return {"threads": T,
+            "quantize_asym_g32_GBps": round(qr / 1e9, 4),
+            "dequantize_asym_g32_bf16_GBps": round(dr / 1e9, 4),
+            "gemm_reference_fp64_GFLOPs": round(fr / 1e9, 4),
+            "sample": f"INT4-asym g32, K = 4096: blocks of {rows} weight rows (codec); "
+                      f"64 x rows x 256 weight rows per GEMM sample; about {seconds:.1f}s each"}
 
 
 if __name__ == "__main__":
