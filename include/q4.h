@@ -78,8 +78,12 @@
  *   - Ownership: every buffer is device memory owned by the caller.  The
  *     library never allocates, frees or retains memory, keeps no state
  *     between calls and never synchronises; it only enqueues kernels on
- *     `stream` (a hipStream_t; NULL selects the null stream).  Its only
- *     globals are read-only constant tables, so calls are thread-safe.
+ *     `stream` (a hipStream_t; NULL selects the null stream).  Its globals
+ *     are read-only constant tables, plus the per-GPU sync words of
+ *     q4_gemv_chain_static (a static device array, and a host table of their
+ *     addresses filled once per device under a lock); every other call is
+ *     thread-safe, and overlapping q4_gemv_chain_static calls on one GPU
+ *     race (see there).
  *   - Errors: every call validates its arguments on the host, before any HIP
  *     call, and returns a q4_status.  Nothing aborts and no C++ exception
  *     crosses the ABI.  Faults inside a kernel surface at the caller's next
