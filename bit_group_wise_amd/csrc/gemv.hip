@@ -28,23 +28,20 @@
 //    a pair of 16-bit weights.  The table is replicated per 32 lane slots (a
 //    lane reads only its own banks) and a byte's LDS address is one
 //    v_perm_b32 (code byte -> address bits 8..15, lane slot -> bits 3..7).
-//  * Multiply-accumulate on the matrix cores, as lane-own dot products: in
-//    v_mfma_f32_4x4x4_16b (16 independent 4 x 4 x 4 blocks, block b on lanes
-//    4b .. 4b + 3) lane 4b + i holds row i of the first operand and column
-//    i of the second, so output (i, i) of block b -- register i of lane
-//    4b + i -- is the dot product of that lane's own 4 weights and 4
-//    activations; the other outputs are never read.  A code dword (8
-//    weights) takes two of them per activation row.  (The 16 x 16 x 32
-//    product with the same diagonal use does 4 times the multiply-adds for
-//    the same sums; the chip runs the weight stream at the power limit, and
-//    the smaller product measured 2-4 % faster.)  The vector ALUs only
-//    dequantize.  M = 2 runs one product per activation row.
+//  * Multiply-accumulate on the vector ALUs in binary32: v_dot2_f32_bf16 /
+//    v_dot2_f32_f16 multiply a pair of 16-bit weights by a pair of 16-bit
+//    activations (both products exact in binary32) and add them to a
+//    binary32 accumulator.  Each activation row keeps two accumulators that
+//    take alternate weight pairs, so consecutive dot2 do not wait on each
+//    other.  (A lane-own form on the 4 x 4 x 4
+//    matrix-core blocks, which takes the dot products off the vector ALUs,
+//    measured the same speed on the decode token: 4503 against 4505 GB/s.)
 //  * Activations: for M = 1 and rows that fit one stage (K <= 4096) each lane
 //    keeps its slices in registers; else, for M <= 2, they are staged once
 //    per workgroup in LDS (rows padded to whole stages with zeros, 16 bytes
 //    of skew per 64-byte chunk so the 16-byte reads of a wave do not collide
 //    in banks); larger K reads them from L2 step by step.
-//  * At the end of a row each lane's own sum (register lane % 4) is summed
+//  * At the end of a row each lane's two accumulators are added and summed
 //    across the wave with DPP; y is rounded once to the activation dtype.
 //  * NF4 with double-quantized absmax ("Loading a model in 4-bit", "Where
 //    the accuracy goes"): a chunk's scale is read as its group's 8-bit code
@@ -55,7 +52,6 @@
 
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
-#include "q4_mfma.hpp"
 
 namespace q4 {
 namespace {
@@ -341,15 +337,26 @@ __device__ __forceinline__ void load_x(u32x4 (&xv)[MT], const uint32_t *xs,
     }
 }
 
-// Sum over the wave of the lanes' own dot products: lane l's is register
-// l % 4 of its accumulator (output (i, i) of its 4 x 4 block).  Every lane
-// gets the total.  (Selects by per-lane conditions, so no branch.)
-__device__ __forceinline__ float diag_sum(const f32x4 &a, int lane)
+// acc += the dot product of 8 weights and 8 activations (16-bit values,
+// packed in pairs): four v_dot2, alternating between the two accumulators.
+template <int ACT>
+__device__ __forceinline__ void dot8(const u32x4 &w, const u32x4 &x, float2 &acc)
 {
-    const float a01 = (lane & 1) ? a[1] : a[0];
-    const float a23 = (lane & 1) ? a[3] : a[2];
-    return wave_sum((lane & 2) ? a23 : a01);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float &a = (k & 1) ? acc.y : acc.x;
+        if constexpr (ACT == Q4_BF16)
+            a = __builtin_amdgcn_fdot2_f32_bf16(std::bit_cast<bf16x2>(w[k]), std::bit_cast<bf16x2>(x[k]), a,
+                                                false);
+        else
+            a = __builtin_amdgcn_fdot2(std::bit_cast<f16x2>(w[k]), std::bit_cast<f16x2>(x[k]), a, false);
+    }
 }
+
+// Sum over the wave of the lanes' two accumulators; every lane gets the total.
+__device__ __forceinline__ float row_sum(const float2 &a) { return wave_sum(a.x + a.y); }
 
 // Table lookups of one code dword: the binary32 level pairs of its 4 bytes.
 __device__ __forceinline__ void lookup4(uint32_t w, uint32_t laneoff, const uint32_t *__restrict__ tbl,
@@ -366,13 +373,13 @@ __device__ __forceinline__ void lookup4(uint32_t w, uint32_t laneoff, const uint
 // Products of one stage: 8 steps of 8 weights (two chunks x four dwords of
 // codes).  Per code byte: its LDS address by one v_perm, one 8-byte table
 // read (the two nibbles' binary32 levels), two fma with the chunk's scale
-// and bias and one packed conversion to the activation dtype; per dword two
-// 4 x 4 x 4 matrix-core products per activation row.  The lookups of the next dword
+// and bias, one packed conversion to the activation dtype and one v_dot2
+// per activation row.  The lookups of the next dword
 // are issued before the current one is converted (scheduling barriers keep
 // that order), so a table read's latency hides behind a dword of
 // arithmetic.
 template <int FMT, int ACT, int MT, int XS>
-__device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
+__device__ __forceinline__ void compute_stage(const Stage &st, float2 (&acc)[MT],
                                               const uint32_t *__restrict__ tbl, const uint32_t *xs,
                                               const u32x4 (&xreg)[XS == X_REG ? 8 * MT : 1],
                                               __amdgpu_buffer_rsrc_t xr, int K, int xrow, int s,
@@ -451,7 +458,7 @@ __device__ __forceinline__ void compute_stage(const Stage &st, f32x4 (&acc)[MT],
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[m] = own_dot8<ACT>(wf, xv[m], acc[m]);
+            dot8<ACT>(wf, xv[m], acc[m]);
         if (t < 7) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -580,10 +587,10 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
         }
     }
 
-    f32x4 acc[MT];
+    float2 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-        acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc[m] = float2{0.0f, 0.0f};
 
     // A round of the ring is never left in the middle (the load waits stay
     // partial only if every path refills every slot): a position past the
@@ -612,8 +619,8 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
                 float out = 0.0f;
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const float t = diag_sum(acc[m], lane);
-                    acc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const float t = row_sum(acc[m]);
+                    acc[m] = float2{0.0f, 0.0f};
                     if (lane == m)
                         out = t;
                 }
@@ -1081,7 +1088,7 @@ void gemv_chain_kernel(const ChainArgs a)
         };
 
         u32x4 xreg[8];
-        f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        float2 acc[1] = {float2{0.0f, 0.0f}};
         int turn = 0;  // blocked walk: the block's rows before this task, mod 15
         const int t0 = has_rows ? tlo : nt;
         for (int t = t0; t <= thi; ++t) {
@@ -1147,8 +1154,8 @@ void gemv_chain_kernel(const ChainArgs a)
                                                           0, laneoff, a.gshift);
                     }
                     if (cp.s == S - 1 && cp.row < end) {
-                        const float out = diag_sum(acc[0], lane);
-                        acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        const float out = row_sum(acc[0]);
+                        acc[0] = float2{0.0f, 0.0f};
                         // through a global (not flat) pointer: a flat store
                         // may write LDS, so LDS reads after it would wait
                         auto *const yp = (__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row);

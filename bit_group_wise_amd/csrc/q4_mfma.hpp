@@ -31,26 +31,6 @@ __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, f32x4 c)
                                                       std::bit_cast<f16x8>(b), c, 0, 0, 0);
 }
 
-// Lane-own dot products on v_mfma_f32_4x4x4_16b: lane 4b + i is row i of
-// block b's first operand and column i of its second, so register i of that
-// lane accumulates the dot product of the lane's own 4 + 4 values (the
-// other registers take cross terms, never read).  a and b are 8 values of
-// the dtype each (two products).
-template <int ACT>
-__device__ __forceinline__ f32x4 own_dot8(const u32x4 &a, const u32x4 &b, f32x4 c)
-{
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-    const u32x2 a0{a[0], a[1]}, a1{a[2], a[3]}, b0{b[0], b[1]}, b1{b[2], b[3]};
-    if constexpr (ACT == Q4_BF16) {
-        c = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(std::bit_cast<s16x4>(a0), std::bit_cast<s16x4>(b0), c, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(std::bit_cast<s16x4>(a1), std::bit_cast<s16x4>(b1), c, 0, 0, 0);
-    } else {
-        c = __builtin_amdgcn_mfma_f32_4x4x4f16(std::bit_cast<h16x4>(a0), std::bit_cast<h16x4>(b0), c, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_4x4x4f16(std::bit_cast<h16x4>(a1), std::bit_cast<h16x4>(b1), c, 0, 0, 0);
-    }
-}
-
 // The 8 weights of one code dword as binary32 values (element i of the
 // dword in v[i]), each the product q4_dequantize rounds.  For NF4 (also with
 // double-quantized absmax, s then being the recovered absmax) the level
