@@ -637,21 +637,27 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 //
 // The weights never depend on earlier tasks, so each compute wave's ring of
 // in-flight weight loads runs on across task boundaries.  Only x may depend
-// on earlier tasks.  A workgroup is 15 compute waves and one loader wave.
-// x sits in LDS in 8 slots of one stage each (8 KB); task t's stages take
-// consecutive slots from slot base_t on (mod 8), tasks in turn, so a slot is
-// reused only by a task at least two later.  The loader copies x of task t
-// (by DMA, as early as the slots allow) once every compute wave has entered
-// the task after the last one that used those slots (the gate, computed on
-// the host) and publishes it; a compute wave entering task t waits only for
-// that.  So waves may drift several tasks apart.  With no task waiting for
-// earlier outputs, each workgroup works on one contiguous block of the
-// tasks' rows and loads and enters only the block's tasks.  Otherwise every
-// task's rows are spread over all waves, and for a task that reads earlier
-// outputs the loader first waits until every compute wave has finished the
-// earlier tasks, then for the whole grid (a grid barrier between loader
-// waves).  The compute waves never wait for each other.  The table is
-// filled once per launch.
+// on earlier tasks.  x sits in LDS in 8 slots of one stage each (8 KB);
+// task t's stages take consecutive slots from slot base_t on (mod 8), tasks
+// in turn, so a slot is reused only by a task at least two later.  x of
+// task t is copied in (by DMA) once every compute wave has entered the task
+// after the last one that used those slots (the gate, computed on the host)
+// and then published; a compute wave entering task t waits only for that.
+//  * With no task waiting for earlier outputs, a workgroup is 15 compute
+//    waves and one loader wave, which copies x as early as the gates allow,
+//    so waves may drift several tasks apart; each workgroup works on one
+//    contiguous block of the tasks' rows and loads and enters only the
+//    block's tasks.
+//  * Otherwise every task's rows are spread over all waves of the grid, and
+//    all 16 waves of a workgroup compute: 4096 waves on 256 units, so that
+//    the 4096-row products of a decode layer give every wave one row (with
+//    15 compute waves, 256 of the 3840 waves took a second row, and a task
+//    ended one row later).  The last wave also moves x, when it enters a
+//    task, after its own weight loads for the task are out: for a task that
+//    reads earlier outputs it first waits until every wave of the workgroup
+//    has finished the earlier tasks, then for the whole grid (a grid barrier
+//    between these waves).
+// The table is filled once per launch.
 struct ChainTask {
     const uint16_t *x;
     const uint8_t *codes;
@@ -877,7 +883,7 @@ __device__ __forceinline__ void wait_vm_upto(int n)
         wait_vm<0>();
 }
 
-constexpr int kChainCompute = 15;  // compute waves per workgroup (wave 15 loads x)
+constexpr int kChainCompute = 15;  // compute waves per workgroup without waiting tasks
 
 // DEP: some task waits for earlier outputs (else the grid-barrier code is
 // left out).
@@ -904,10 +910,10 @@ void gemv_chain_kernel(const ChainArgs a)
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const int nt = a.ntasks;
+    constexpr int NC = DEP ? 16 : kChainCompute;  // compute waves
     // every compute wave has entered task t
     auto all_entered = [&](int t) {
-        return __hip_atomic_load(&entered[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >=
-               kChainCompute;
+        return __hip_atomic_load(&entered[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NC;
     };
     auto fail = [&]() {
         __hip_atomic_store(&a.sync[kSyncTimeout], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -974,12 +980,11 @@ void gemv_chain_kernel(const ChainArgs a)
     // the tasks this workgroup loads and enters: tlo .. thi
     const int thi = !has_rows ? tlo - 1 : (rend == 0 ? tend - 1 : tend);
 
-    if (wave == kChainCompute) {
+    if (!DEP && wave == kChainCompute) {
         // ---------------------------------------------------------- loader
         // x goes in by DMA as early as the slots allow: a later task's as
-        // soon as its gate is open (unless it reads earlier outputs), up to
-        // kChainDmaAhead instructions ahead; the current task's is then
-        // awaited and published.
+        // soon as its gate is open, up to kChainDmaAhead instructions ahead;
+        // the current task's is then awaited and published.
         int issued = 0;  // tasks whose x DMA is issued (in order)
         int ahead = 0;   // DMA instructions in flight for tasks after the current one
         auto dma_count = [&](const ChainTask &T) { return kChainDmaPerStage * chain_stages(T.K); };
@@ -987,7 +992,7 @@ void gemv_chain_kernel(const ChainArgs a)
             while (issued <= thi) {
                 const ChainTask T = task(issued);
                 const int n = dma_count(T);
-                if ((DEP && ctl_wait(T.ctl)) || ahead + n > kChainDmaAhead || !all_entered(ctl_gate(T.ctl)))
+                if (ahead + n > kChainDmaAhead || !all_entered(ctl_gate(T.ctl)))
                     break;
                 chain_dma_x(T, xb, lane);
                 ahead += n;
@@ -1012,7 +1017,6 @@ void gemv_chain_kernel(const ChainArgs a)
             publish(tlo);
         }
         __syncthreads();  // the table, the counters and x of task tlo
-        int nbar = 0;
         for (int t = tlo + 1; t <= thi; ++t) {
             const ChainTask T = task(t);
             if (issued > t) {
@@ -1020,25 +1024,16 @@ void gemv_chain_kernel(const ChainArgs a)
             } else {
                 // the slots of task t last held x of an earlier task: wait
                 // until every compute wave has entered the task after it
-                // (the gate); a task that reads earlier outputs waits until
-                // they have finished t - 1 (entered t, stores complete).
-                // Nothing is in flight here.
-                const bool wait = DEP && ctl_wait(T.ctl);
-                const int need = wait ? t : ctl_gate(T.ctl);
+                // (the gate).  Nothing is in flight here.
                 uint32_t spins = 0;
-                while (!all_entered(need)) {
+                while (!all_entered(ctl_gate(T.ctl))) {
                     if (++spins == kSpinLimit) {
                         fail();
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
                 }
-                if (wait) {
-                    grid_barrier(a.sync, ++nbar, lane, fail);
-                    chain_dma_x<kCoherent>(T, xb, lane);  // earlier outputs
-                } else {
-                    chain_dma_x(T, xb, lane);
-                }
+                chain_dma_x(T, xb, lane);
                 issued = t + 1;
             }
             issue_ahead();
@@ -1055,14 +1050,29 @@ void gemv_chain_kernel(const ChainArgs a)
         // to task.  Inside a segment the ring is the single-product
         // kernel's: a position is a row and a stage, advanced with a few
         // scalar instructions; task switches stay out of that loop.
-        const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * kChainCompute + wave);
+        const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * NC + wave);
         const LaneOffs lo = lane_offs<FMT>(lane, a.gshift);
-        const int total_waves = gridDim.x * kChainCompute;
+        const int total_waves = gridDim.x * NC;
+        // with waiting tasks the last wave also moves x: task tlo's here,
+        // every later task's when it enters the task (lead_x)
+        const bool lead = DEP && wave == NC - 1;
+        if (lead) {
+            // task tlo is entered by every compute wave in the prologue; the
+            // tasks before it are never entered here (none, with waits)
+            entered[lane] = lane <= tlo ? NC : 0;
+            ready[lane] = 0;
+            if (has_rows) {
+                chain_dma_x(task(tlo), xb, lane);
+                wait_vm<0>();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __hip_atomic_store(&ready[tlo], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
         __syncthreads();  // the table, the counters and x of task tlo
         int cur = tlo;  // the last task this wave has counted into
         // Counting into task t (this wave is done with every earlier task).
         // Before a task that reads earlier outputs, this wave's own stores
-        // complete first (the loader then passes them on to the grid): with
+        // complete first (the lead wave then passes them on to the grid): with
         // the count taken before the task's first weight loads go out, the
         // wait covers the stores alone.
         auto arrive = [&](int t) {
@@ -1086,6 +1096,35 @@ void gemv_chain_kernel(const ChainArgs a)
             }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
         };
+        // (lead wave) x of task t into its slots, then published: once every
+        // compute wave has entered the task's gate, or, for a task that reads
+        // earlier outputs, has entered t (finished t - 1, stores complete)
+        // and every workgroup has passed the grid barrier.  The lead wave's
+        // own weight loads for t are out by then; the wait before publishing
+        // covers them too.
+        int nbar = 0;
+        auto lead_x = [&](int t) {
+            const ChainTask T = task(t);
+            const bool wait = ctl_wait(T.ctl);
+            const int need = wait ? t : ctl_gate(T.ctl);
+            uint32_t spins = 0;
+            while (!all_entered(need)) {
+                if (++spins == kSpinLimit) {
+                    fail();
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (wait) {
+                grid_barrier(a.sync, ++nbar, lane, fail);
+                chain_dma_x<kCoherent>(T, xb, lane);  // earlier outputs
+            } else {
+                chain_dma_x(T, xb, lane);
+            }
+            wait_vm<0>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __hip_atomic_store(&ready[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
 
         u32x4 xreg[8];
         float2 acc[1] = {float2{0.0f, 0.0f}};
@@ -1108,8 +1147,11 @@ void gemv_chain_kernel(const ChainArgs a)
             }
             while (cur < t)
                 arrive(++cur);
-            if (first >= end)
+            if (first >= end) {
+                if (lead && t > tlo)
+                    lead_x(t);
                 continue;  // no rows here
+            }
             const int S = tv.S;
             // positions: rows first, first + step, ...; a row at or past end
             // loads from an empty view (zeros) and stores nothing
@@ -1134,6 +1176,8 @@ void gemv_chain_kernel(const ChainArgs a)
                     pos[q] = advance(pos[q - 1]);
                 load_pos(st[q], pos[q]);
             }
+            if (lead && t > tlo)
+                lead_x(t);
             await_x(t);
             if (S == 1)
                 chain_x_slice(xreg, xb, tv.xbase, 0, lane);
