@@ -156,10 +156,11 @@ q4_status q4_dequantize(q4_format f, int g, const uint8_t *codes, const void *sc
  * accumulation, one rounding of y to act_t.  Every weight enters as the
  * value q4_dequantize writes in act_t, so the result equals a 16-bit matmul
  * on the dequantized weights up to summation order ("Where the accuracy
- * goes").  M = 1, 2 dequantize on the vector ALUs with one row per wave;
- * 3 <= M <= 16 run as a skinny product over blocks of 16 rows; both
- * multiply on the matrix cores.  M > 16 returns Q4_EUNSUPPORTED (use
- * q4_gemm); K > Q4_GEMV_MAX_K returns Q4_EUNSUPPORTED. */
+ * goes").  M = 1, 2 dequantize and multiply on the vector ALUs (binary32
+ * dot products of 16-bit pairs) with one row per wave; 3 <= M <= 16 run as
+ * a skinny product over blocks of 16 rows on the matrix cores.  M > 16
+ * returns Q4_EUNSUPPORTED (use q4_gemm); K > Q4_GEMV_MAX_K returns
+ * Q4_EUNSUPPORTED. */
 #define Q4_GEMV_MAX_K 33554432
 q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                   const uint8_t *codes, const void *scales, const uint8_t *zeros,
