@@ -13,10 +13,10 @@
 // one dword, so a wave reads 1 KB and writes 256 B per step, fully
 // coalesced.  A group spans g/8 adjacent lanes and is reduced with
 // cross-lane shuffles.  The quotient w / s is formed from one correctly
-// rounded reciprocal per group plus Markstein's correction (q0 = w*r;
-// e = fma(-q0, s, w); q = fma(e, r, q0)), which equals the correctly rounded
-// IEEE quotient for every pair of fp16 operands with s > 0 (checked
-// exhaustively on all such pairs); NF4 codes come from a 33-bucket table of
+// rounded reciprocal per group (rcp_rn) plus Markstein's correction
+// (q0 = w*r; e = fma(-q0, s, w); q = fma(e, r, q0)), which equals the
+// correctly rounded IEEE quotient for every pair of fp16 operands with s > 0
+// (checked exhaustively on all such pairs); NF4 codes come from a 33-bucket table of
 // exact decision thresholds held in LDS, FP4 codes from seven exact
 // thresholds on the magnitude and the sign.
 //
@@ -48,6 +48,29 @@ __device__ __forceinline__ float div_mk(float a, float b, float r)
     return __builtin_fmaf(e, r, q0);
 }
 
+// The scale quotients a / 7 (INT4-sym, a the absmax) and (hi - lo) / 15
+// (INT4-asym) with the constant reciprocals RN(1/7) and RN(1/15): three
+// instructions instead of a general division.  Equal to the IEEE quotient
+// for every operand these can meet (a any non-negative fp16 value; hi - lo
+// rounded to binary32 for any non-negative fp16 hi and non-positive fp16 lo),
+// checked exhaustively.
+constexpr float kInv7 = 1.0f / 7.0f;
+constexpr float kInv15 = 1.0f / 15.0f;
+
+// RN(1 / s) for s > 0 an fp16 value (the stored scale, or the absmax): the
+// hardware reciprocal (accurate to 1 ulp) and one Newton step,
+// r = r0 + r0 * (1 - s * r0) with both steps fused.  The step leaves a
+// relative error of order 2^-46, while 1 / s, whose divisor has at most 11
+// significant bits, lies at least 2^-35 (relative) away from any rounding
+// midpoint, so the result is the correctly rounded reciprocal; checked
+// exhaustively for every positive fp16 s and every start within 2 ulps.
+__device__ __forceinline__ float rcp_rn(float s)
+{
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-r0, s, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
 template <int LPG>
 __device__ __forceinline__ float group_max(float v)
 {
@@ -69,7 +92,7 @@ __device__ __forceinline__ float group_min(float v)
 // nibble first).
 __device__ __forceinline__ uint32_t nf4_word(const float (&v)[8], float c, const NF4Bucket *lut)
 {
-    const float r = 1.0f / c;
+    const float r = rcp_rn(c);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -89,7 +112,7 @@ __device__ __forceinline__ uint32_t nf4_word(const float (&v)[8], float c, const
 // (code j + 8 for x < 0 and j > 0; the tie of +0 and -0 keeps code 0).
 __device__ __forceinline__ uint32_t fp4_word(const float (&v)[8], float c)
 {
-    const float r = 1.0f / c;
+    const float r = rcp_rn(c);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -162,10 +185,12 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
                 for (int i = 0; i < 8; ++i)
                     a = fmaxf(a, fabsf(v[i]));
                 a = group_max<LPG>(a);
-                const uint32_t s16 = f2h_bits(a / 7.0f);
+                // (the quotient rounded to binary32 first, then to fp16: no
+                // single-rounding mixed fma)
+                const uint32_t s16 = f2h_bits(keep_f32(div_mk(a, 7.0f, kInv7)));
                 const float s = h2f(s16);
                 if (s != 0.0f) {
-                    const float r = 1.0f / s;
+                    const float r = rcp_rn(s);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         int q = (int)__builtin_rintf(div_mk(v[i], s, r));
@@ -186,11 +211,11 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
                 }
                 lo = group_min<LPG>(lo);
                 hi = group_max<LPG>(hi);
-                const uint32_t s16 = f2h_bits((hi - lo) / 15.0f);
+                const uint32_t s16 = f2h_bits(keep_f32(div_mk(hi - lo, 15.0f, kInv15)));
                 const float s = h2f(s16);
                 int z = 0;
                 if (s != 0.0f) {
-                    const float r = 1.0f / s;
+                    const float r = rcp_rn(s);
                     z = (int)__builtin_rintf(div_mk(-lo, s, r));
                     z = z < 0 ? 0 : (z > 15 ? 15 : z);
 #pragma unroll
