@@ -71,6 +71,34 @@ __device__ __forceinline__ float rcp_rn(float s)
     return __builtin_fmaf(e, r0, r0);
 }
 
+// INT4 codes q = clamp(rint(x) + z, 0, 15) for any finite x (here x = w / s).
+// For |x| < 2^22, adding 1.5 * 2^23 rounds x to an integer exactly as rint
+// does (to nearest, ties to even: the sum's unit is 1) and leaves it in the
+// low bits of the sum's bit pattern, kRintBias + rint(x); a larger |x| puts
+// the sum beyond the clamp below, on the side the clamp of rint(x) + z takes
+// too (and |w / s| <= 23 for finite fp16 inputs anyway).  Clamping the sum to
+// [1.5 * 2^23 - z, 1.5 * 2^23 + 15 - z] (v_med3; integers there are exact)
+// leaves kRintBias - z + q in the bits, so the instructions per weight are
+// one add, one clamp and the packing; the offset kRintBias - z comes off
+// once per dword (pack8).
+constexpr float kRint = 12582912.0f;         // 1.5 * 2^23
+constexpr uint32_t kRintBias = 0x4B400000u;  // its bit pattern
+__device__ __forceinline__ uint32_t code_bits(float x, float lo, float hi)
+{
+    return std::bit_cast<uint32_t>(__builtin_amdgcn_fmed3f(x + kRint, lo, hi));
+}
+// 8 codes as one dword, low nibble first, from code_bits values c = off + q:
+// shifted and added (codes below 16 never carry into the next nibble), then
+// the offsets' shifted sum, off * 0x11111111 mod 2^32, taken off.
+__device__ __forceinline__ uint32_t pack8(const uint32_t (&c)[8], uint32_t off)
+{
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        word += c[i] << (4 * i);
+    return word - off * 0x11111111u;
+}
+
 template <int LPG>
 __device__ __forceinline__ float group_max(float v)
 {
@@ -191,12 +219,12 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
                 const float s = h2f(s16);
                 if (s != 0.0f) {
                     const float r = rcp_rn(s);
+                    // q = clamp(rint(w / s), -8, 7) + 8: z = 8
+                    uint32_t c[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        int q = (int)__builtin_rintf(div_mk(v[i], s, r));
-                        q = q < -8 ? -8 : (q > 7 ? 7 : q);
-                        word |= (uint32_t)(q + 8) << (4 * i);
-                    }
+                    for (int i = 0; i < 8; ++i)
+                        c[i] = code_bits(div_mk(v[i], s, r), kRint - 8.0f, kRint + 7.0f);
+                    word = pack8(c, kRintBias - 8u);
                 } else {
                     word = 0x88888888u;
                 }
@@ -218,12 +246,12 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4 *__restric
                     const float r = rcp_rn(s);
                     z = (int)__builtin_rintf(div_mk(-lo, s, r));
                     z = z < 0 ? 0 : (z > 15 ? 15 : z);
+                    const float lo_c = kRint - (float)z;
+                    uint32_t c[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        int q = (int)__builtin_rintf(div_mk(v[i], s, r)) + z;
-                        q = q < 0 ? 0 : (q > 15 ? 15 : q);
-                        word |= (uint32_t)q << (4 * i);
-                    }
+                    for (int i = 0; i < 8; ++i)
+                        c[i] = code_bits(div_mk(v[i], s, r), lo_c, lo_c + 15.0f);
+                    word = pack8(c, kRintBias - (uint32_t)z);
                 }
                 // zero-points: the leader of an even group packs its own and
                 // the next group's (LPG lanes further on; both groups lie in
