@@ -125,9 +125,10 @@ __device__ __forceinline__ uint32_t nf4_word(const float (&v)[8], float c, const
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float x = div_mk(v[i], c, r);
-        // |x| <= 1, so b <= 32; the min only guards inputs that break the
-        // finite-input precondition
-        const uint32_t b = min((uint32_t)((x + 1.0f) * 16.0f), 32u);
+        // bucket floor((x + 1) * 16), the product formed as one fma (16 (x + 1)
+        // rounds as x + 1 does, scaled exactly); |x| <= 1, so b <= 32; the min
+        // only guards inputs that break the finite-input precondition
+        const uint32_t b = min((uint32_t)__builtin_fmaf(x, 16.0f, 16.0f), 32u);
         const NF4Bucket e = lut[b];
         const uint32_t code = e.base + (x >= e.thr ? 1u : 0u);
         word |= code << (4 * i);
