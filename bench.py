@@ -52,6 +52,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+WARM_MC = 400                # warm-up calls of the matrix-core legs
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, TFLOP/s
 
 LAYERS = 32
@@ -589,9 +590,11 @@ def extra_legs(torch, q4, dev, stream):
     out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     dt = timed(lambda: q4.dequantize(q, torch.bfloat16, out=out), 10)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    # matrix-core legs: steady state after 20 warm-up calls (the first
-    # calls after idle run at a lower clock)
-    gt = timed(lambda: q4.gemm(x, q, out=y), 30, warm=20)
+    # matrix-core legs: steady state after 400 warm-up calls (about 0.1 s;
+    # the first calls after a change of load run at a lower clock: the
+    # M = 2048 GEMM took 257 us per call over its first 5 ms and 215 us after
+    # 30 ms), the fused and the unfused legs alike
+    gt = timed(lambda: q4.gemm(x, q, out=y), 30, warm=WARM_MC)
     flops = 2.0 * M * N * K
     codec_bytes = N * K * 2 + q.nbytes()
     # the pages' unfused path: dequantize to the compute dtype, then a
@@ -601,8 +604,8 @@ def extra_legs(torch, q4, dev, stream):
     def unfused():
         q4.dequantize(q, torch.bfloat16, out=out)
         torch.matmul(x, out.t(), out=yb)
-    ut = timed(unfused, 30, warm=20)
-    mt = timed(lambda: torch.matmul(x, out.t(), out=yb), 30, warm=20)
+    ut = timed(unfused, 30, warm=WARM_MC)
+    mt = timed(lambda: torch.matmul(x, out.t(), out=yb), 30, warm=WARM_MC)
     # the same at decode width: M = 16 on the c3 gate/up shape (NF4 g64)
     w16 = torch.empty((11008, 4096), dtype=torch.float16, device=dev).normal_(0.0, 0.02)
     q16 = q4.quantize(w16, q4.NF4, 64)
@@ -622,12 +625,12 @@ def extra_legs(torch, q4, dev, stream):
     dy = torch.empty((M, N), dtype=torch.float32, device=dev).normal_(0.0, 1.0, generator=gen)
     dy = dy.to(torch.bfloat16)
     dxo = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    bt = timed(lambda: q4.gemm_dx(dy, q, out=dxo), 30, warm=20)
+    bt = timed(lambda: q4.gemm_dx(dy, q, out=dxo), 30, warm=WARM_MC)
 
     def unfused_dx():
         q4.dequantize(q, torch.bfloat16, out=out)
         torch.matmul(dy, out, out=dxo)
-    but = timed(unfused_dx, 30, warm=20)
+    but = timed(unfused_dx, 30, warm=WARM_MC)
     return {
         "gemm_dx": {"shape": f"dY {M}x{N} . W {N}x{K} int4_asym g32 bf16", "ms": round(bt, 4),
                     "TFLOPs": round(flops / (bt * 1e-3) / 1e12, 1),
