@@ -397,7 +397,8 @@ def _prefill_inputs(torch, q4, dev):
 
 
 def one_leg(leg, torch, q4, dev, stream):
-    """One leg alone, 5 timed repetitions (for profiler runs)."""
+    """One leg alone, 5 timed repetitions (for profiler runs; the matrix-core
+    legs after the same warm-up as in the full run)."""
     timed = _timer(torch, stream)
     if leg == "copy":
         n = 1 << 30
@@ -425,11 +426,11 @@ def one_leg(leg, torch, q4, dev, stream):
     if leg == "gemm_dx":
         dy = torch.randn((M, N), device=dev).to(torch.bfloat16)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        ms = timed(lambda: q4.gemm_dx(dy, q, out=dx), 5)
+        ms = timed(lambda: q4.gemm_dx(dy, q, out=dx), 5, warm=WARM_MC)
         return {"leg": leg, "ms": round(ms, 4),
                 "TFLOPs": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ms = timed(lambda: q4.gemm(x, q, out=y), 5)
+    ms = timed(lambda: q4.gemm(x, q, out=y), 5, warm=WARM_MC)
     return {"leg": "gemm", "ms": round(ms, 4),
             "TFLOPs": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
 
