@@ -714,7 +714,8 @@ static_assert(4 * (kSyncFlag + kSyncLine) == Q4_GEMV_CHAIN_SYNC_BYTES, "sync buf
 // use), so no dirty or stale copy of it sits in any one XCD's L2.  What is
 // left is order: a compute wave waits for its output stores to complete
 // (s_waitcnt vmcnt(0)) before it counts into the next task in LDS; the
-// loader arrives only after every compute wave has; the last arrival of a
+// workgroup's last wave, which moves x in a chain with waits, arrives only
+// after every compute wave has; the last arrival of a
 // group and the flag store follow the counter's atomic return; the x
 // loads go out after a flag poll has returned.  Each step starts after the
 // previous one has completed, so the outputs are at the coherence point
@@ -838,9 +839,10 @@ constexpr int kChainDmaPerStage = 8;
 // multiple of kChainDmaPerStage, within the vector-memory counter's range).
 constexpr int kChainDmaAhead = 40;
 
-// The loader's copy of x[0, K) of a task into the task's slots, by the
-// buffer unit straight into LDS (no registers, so the loader can have
-// several tasks in flight): per stage, half and piece, one 16-byte load per
+// The copy of x[0, K) of a task into the task's slots (by the loader wave, or
+// with waiting tasks by the workgroup's last wave), by the buffer unit
+// straight into LDS (no registers, so the loader can have several tasks in
+// flight): per stage, half and piece, one 16-byte load per
 // lane, lane l's piece j of chunk c0 + l landing at 16-byte index
 // 128 j + c0 + l of the slot, the piece-major order the compute waves read.
 // The whole offset is the lane's (voffset, range-checked against the x
