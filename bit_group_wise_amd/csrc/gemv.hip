@@ -643,20 +643,22 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 // task t is copied in (by DMA) once every compute wave has entered the task
 // after the last one that used those slots (the gate, computed on the host)
 // and then published; a compute wave entering task t waits only for that.
-//  * With no task waiting for earlier outputs, a workgroup is 15 compute
-//    waves and one loader wave, which copies x as early as the gates allow,
-//    so waves may drift several tasks apart; each workgroup works on one
+// All 16 waves of a workgroup compute; the last one also moves x, when it
+// enters a task, after its own weight loads for the task are out.  (A
+// separate loader wave, which copied x as early as the gates allowed, left
+// its SIMD a wave short of the others: 16 compute waves measured 1 % faster
+// on the independent decode token and 8 % on the dependent one.)
+//  * With no task waiting for earlier outputs, each workgroup works on one
 //    contiguous block of the tasks' rows and loads and enters only the
-//    block's tasks.
-//  * Otherwise every task's rows are spread over all waves of the grid, and
-//    all 16 waves of a workgroup compute: 4096 waves on 256 units, so that
-//    the 4096-row products of a decode layer give every wave one row (with
-//    15 compute waves, 256 of the 3840 waves took a second row, and a task
-//    ended one row later).  The last wave also moves x, when it enters a
-//    task, after its own weight loads for the task are out: for a task that
-//    reads earlier outputs it first waits until every wave of the workgroup
-//    has finished the earlier tasks, then for the whole grid (a grid barrier
-//    between these waves).
+//    block's tasks, so a workgroup meets a new task once or twice per
+//    launch.
+//  * Otherwise every task's rows are spread over all waves of the grid:
+//    4096 waves on 256 units, so that the 4096-row products of a decode
+//    layer give every wave one row (with 15 compute waves, 256 of the 3840
+//    waves took a second row, and a task ended one row later).  For a task
+//    that reads earlier outputs the last wave first waits until every wave
+//    of the workgroup has finished the earlier tasks, then for the whole
+//    grid (a grid barrier between these waves).
 // The table is filled once per launch.
 struct ChainTask {
     const uint16_t *x;
@@ -714,8 +716,8 @@ static_assert(4 * (kSyncFlag + kSyncLine) == Q4_GEMV_CHAIN_SYNC_BYTES, "sync buf
 // use), so no dirty or stale copy of it sits in any one XCD's L2.  What is
 // left is order: a compute wave waits for its output stores to complete
 // (s_waitcnt vmcnt(0)) before it counts into the next task in LDS; the
-// workgroup's last wave, which moves x in a chain with waits, arrives only
-// after every compute wave has; the last arrival of a
+// workgroup's last wave, which moves x, arrives only after every compute
+// wave has; the last arrival of a
 // group and the flag store follow the counter's atomic return; the x
 // loads go out after a flag poll has returned.  Each step starts after the
 // previous one has completed, so the outputs are at the coherence point
@@ -833,18 +835,11 @@ __device__ __forceinline__ ChainTask lds_task(const ChainTask *tasks, int t)
     return T;
 }
 
-// x DMA instructions per stage: 2 halves of 64 chunks, 4 pieces each.
-constexpr int kChainDmaPerStage = 8;
-// x DMA instructions of later tasks the loader keeps in flight at most (a
-// multiple of kChainDmaPerStage, within the vector-memory counter's range).
-constexpr int kChainDmaAhead = 40;
-
-// The copy of x[0, K) of a task into the task's slots (by the loader wave, or
-// with waiting tasks by the workgroup's last wave), by the buffer unit
-// straight into LDS (no registers, so the loader can have several tasks in
-// flight): per stage, half and piece, one 16-byte load per
-// lane, lane l's piece j of chunk c0 + l landing at 16-byte index
-// 128 j + c0 + l of the slot, the piece-major order the compute waves read.
+// The copy of x[0, K) of a task into the task's slots (by the workgroup's
+// last wave), by the buffer unit straight into LDS (no registers): per
+// stage, half and piece, one 16-byte load per lane, lane l's piece j of
+// chunk c0 + l landing at 16-byte index 128 j + c0 + l of the slot, the
+// piece-major order the compute waves read.
 // The whole offset is the lane's (voffset, range-checked against the x
 // view), so pieces past K read zeros: the stored rows are padded to whole
 // stages with zeros.
@@ -866,26 +861,7 @@ __device__ __forceinline__ void chain_dma_x(const ChainTask &T, u32x4 *xb, int l
     }
 }
 
-// Waits until at most n vector-memory instructions (a multiple of
-// kChainDmaPerStage, at most kChainDmaAhead) are in flight.
-__device__ __forceinline__ void wait_vm_upto(int n)
-{
-    static_assert(kChainDmaAhead == 40 && kChainDmaPerStage == 8, "bins below");
-    if (n >= 40)
-        wait_vm<40>();
-    else if (n >= 32)
-        wait_vm<32>();
-    else if (n >= 24)
-        wait_vm<24>();
-    else if (n >= 16)
-        wait_vm<16>();
-    else if (n >= 8)
-        wait_vm<8>();
-    else
-        wait_vm<0>();
-}
-
-constexpr int kChainCompute = 15;  // compute waves per workgroup without waiting tasks
+constexpr int kChainCompute = 16;  // compute waves per workgroup (all of them)
 
 // DEP: some task waits for earlier outputs (else the grid-barrier code is
 // left out).
@@ -912,7 +888,7 @@ void gemv_chain_kernel(const ChainArgs a)
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t laneoff = (uint32_t)(lane & 31) << 3;
     const int nt = a.ntasks;
-    constexpr int NC = DEP ? 16 : kChainCompute;  // compute waves
+    constexpr int NC = kChainCompute;
     // every compute wave has entered task t
     auto all_entered = [&](int t) {
         return __hip_atomic_load(&entered[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= NC;
@@ -982,66 +958,7 @@ void gemv_chain_kernel(const ChainArgs a)
     // the tasks this workgroup loads and enters: tlo .. thi
     const int thi = !has_rows ? tlo - 1 : (rend == 0 ? tend - 1 : tend);
 
-    if (!DEP && wave == kChainCompute) {
-        // ---------------------------------------------------------- loader
-        // x goes in by DMA as early as the slots allow: a later task's as
-        // soon as its gate is open, up to kChainDmaAhead instructions ahead;
-        // the current task's is then awaited and published.
-        int issued = 0;  // tasks whose x DMA is issued (in order)
-        int ahead = 0;   // DMA instructions in flight for tasks after the current one
-        auto dma_count = [&](const ChainTask &T) { return kChainDmaPerStage * chain_stages(T.K); };
-        auto issue_ahead = [&]() {
-            while (issued <= thi) {
-                const ChainTask T = task(issued);
-                const int n = dma_count(T);
-                if (ahead + n > kChainDmaAhead || !all_entered(ctl_gate(T.ctl)))
-                    break;
-                chain_dma_x(T, xb, lane);
-                ahead += n;
-                ++issued;
-            }
-        };
-        auto publish = [&](int t) {
-            wait_vm_upto(ahead);  // task t's DMA is done (they complete in order)
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __hip_atomic_store(&ready[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        };
-        // task tlo is entered by every compute wave in the prologue; the
-        // tasks before it are never entered here (they count as entered,
-        // for the gates of the slots they would have used)
-        entered[lane] = lane <= tlo ? kChainCompute : 0;
-        ready[lane] = 0;
-        issued = tlo;
-        if (has_rows) {
-            chain_dma_x(task(tlo), xb, lane);
-            issued = tlo + 1;
-            issue_ahead();
-            publish(tlo);
-        }
-        __syncthreads();  // the table, the counters and x of task tlo
-        for (int t = tlo + 1; t <= thi; ++t) {
-            const ChainTask T = task(t);
-            if (issued > t) {
-                ahead -= dma_count(T);  // in flight already: now the current task
-            } else {
-                // the slots of task t last held x of an earlier task: wait
-                // until every compute wave has entered the task after it
-                // (the gate).  Nothing is in flight here.
-                uint32_t spins = 0;
-                while (!all_entered(ctl_gate(T.ctl))) {
-                    if (++spins == kSpinLimit) {
-                        fail();
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                chain_dma_x(T, xb, lane);
-                issued = t + 1;
-            }
-            issue_ahead();
-            publish(t);
-        }
-    } else {
+    {
         // ---------------------------------------------------------- compute
         // A wave's walk, task by task: in each task it takes rows first,
         // first + step, ... below end (a segment).  With no waiting task the
@@ -1055,12 +972,13 @@ void gemv_chain_kernel(const ChainArgs a)
         const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * NC + wave);
         const LaneOffs lo = lane_offs<FMT>(lane, a.gshift);
         const int total_waves = gridDim.x * NC;
-        // with waiting tasks the last wave also moves x: task tlo's here,
-        // every later task's when it enters the task (lead_x)
-        const bool lead = DEP && wave == NC - 1;
+        // the last wave also moves x: task tlo's here, every later task's
+        // when it enters the task (lead_x)
+        const bool lead = wave == NC - 1;
         if (lead) {
             // task tlo is entered by every compute wave in the prologue; the
-            // tasks before it are never entered here (none, with waits)
+            // tasks before it are never entered here (they count as entered,
+            // for the gates of the slots they would have used)
             entered[lane] = lane <= tlo ? NC : 0;
             ready[lane] = 0;
             if (has_rows) {
@@ -1107,7 +1025,7 @@ void gemv_chain_kernel(const ChainArgs a)
         int nbar = 0;
         auto lead_x = [&](int t) {
             const ChainTask T = task(t);
-            const bool wait = ctl_wait(T.ctl);
+            const bool wait = DEP && ctl_wait(T.ctl);
             const int need = wait ? t : ctl_gate(T.ctl);
             uint32_t spins = 0;
             while (!all_entered(need)) {
@@ -1130,7 +1048,7 @@ void gemv_chain_kernel(const ChainArgs a)
 
         u32x4 xreg[8];
         float2 acc[1] = {float2{0.0f, 0.0f}};
-        int turn = 0;  // blocked walk: the block's rows before this task, mod 15
+        int turn = 0;  // blocked walk: the block's rows before this task, mod NC
         const int t0 = has_rows ? tlo : nt;
         for (int t = t0; t <= thi; ++t) {
             const ChainTask T = task(t);
@@ -1139,9 +1057,9 @@ void gemv_chain_kernel(const ChainArgs a)
             if constexpr (!DEP) {
                 const int start = t == tlo ? rlo : 0;
                 end = (t == tend) ? rend : tv.N;
-                first = start + (wave - turn + kChainCompute) % kChainCompute;
-                step = kChainCompute;
-                turn = (turn + end - start) % kChainCompute;
+                first = start + (wave - turn + NC) % NC;
+                step = NC;
+                turn = (turn + end - start) % NC;
             } else {
                 first = (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
                 step = total_waves;
