@@ -299,6 +299,7 @@ def main():
         extra["gemv_configs_cold"] = config_gemvs(torch, q4, dev, stream)
         extra["codec_configs_cold"] = codec_configs(torch, q4, dev, stream)
         extra["hbm_copy_ceiling"] = copy_ceiling(torch, dev, stream)
+        extra["hbm_read_ceiling"] = read_ceiling(torch, dev, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -561,6 +562,22 @@ def copy_ceiling(torch, dev, stream):
     return {"bytes_moved": 2 * n, "ms": round(ms, 4),
             "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * 2 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+
+
+def read_ceiling(torch, dev, stream):
+    """A read-only stream: torch's row sums of a 65536 x 16384 fp32 matrix
+    (4 GiB read, 256 KiB written; of the library reductions tried, the
+    fastest reader), beside which a weight stream that reads and barely
+    writes is read (context, not a peak)."""
+    n = 1 << 32
+    a = torch.ones((65536, n // 4 // 65536), dtype=torch.float32, device=dev)
+    out = torch.empty((65536,), dtype=torch.float32, device=dev)
+    ms = _timer(torch, stream)(lambda: torch.sum(a, dim=1, out=out), 10)
+    del a, out
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "ms": round(ms, 4),
+            "GBps": round(n / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
 def config_gemvs(torch, q4, dev, stream):
