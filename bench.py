@@ -23,14 +23,16 @@ launch stream:
   * the one-shot quantize of all weights (HBM-resident fp16 input),
   * dequantize of a 14336x4096 INT4-asym weight to bf16,
   * the prefill GEMM M=2048, N=14336, K=4096, INT4-asym g32, bf16 x
-    (TFLOP/s against the dense bf16 matrix-core peak),
+    (TFLOP/s against the dense bf16 matrix-core peak) and the backward
+    product dX = dY . What on the same weight, after 400 warm-up calls each,
   * the unfused path (dequantize to bf16, then torch.matmul / hipBLASLt) at
     the prefill shape and at M = 16 on an 11008x4096 NF4 weight, beside the
     fused kernels,
   * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
     NF4 g64 1024x1024 and INT4-sym g128 4096x4096 at M = 1, NF4 g64
     11008x4096 and 4096x11008 at M = 1, 4, 16,
-  * a plain 1 GiB device copy, the streaming ceiling read beside the rates,
+  * a plain 1 GiB device copy and a 4 GiB read-only row sum (torch), the
+    streaming ceilings read beside the rates,
   * quantize and dequantize of the single-matrix workloads in their own
     formats on cold buffers,
   * the CPU oracle on a time-bounded sample of the token, on one thread and
