@@ -154,8 +154,9 @@ def _products(fmt, g, act, q, x_bits, oc_os_oz, tag):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("g", [32, 64, 128])
 def test_bf16_midpoint_weights(fmt, g):
-    """The verdict's construction, generalised: bf16 midpoints everywhere,
-    x = +-1 by rounding direction; K spans one and several chain stages."""
+    """Weights at bf16 midpoints everywhere, x = +-1 by rounding direction
+    (so that every rounding gap adds up); K spans one and several chain
+    stages."""
     for N, K in [(24, 2048), (6, 8192 + 2 * g)]:
         w = tie_rows(fmt, g, N, K)
         case, x, gapsum = adversarial_case(fmt, g, q4.BF16, w, 1.0)
@@ -165,7 +166,7 @@ def test_bf16_midpoint_weights(fmt, g):
 
 
 def test_small_nf4_midpoint_row():
-    """The two-block row of the verdict: blocks of 1 + 2^-8 and 1 + 3 * 2^-8,
+    """A two-block NF4 row: blocks of 1 + 2^-8 and 1 + 3 * 2^-8 (bf16 midpoints),
     x = +1 then -1.  The reference is -1.0 (the bf16 weights are 1 and
     1.015625); the scale-hoisted sum would give -0.5."""
     w = np.concatenate([np.full(64, F16_ONE_PLUS[1], np.uint16),
