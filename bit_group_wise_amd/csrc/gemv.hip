@@ -487,6 +487,10 @@ struct Shape {
 struct Pos {
     int row, s;
 };
+// ... and in a chain's walk: task, row and stage.
+struct ChainPos {
+    int t, row, s;
+};
 
 // Each wave walks its rows and, inside a row, the stages along K.  The
 // loads of the next P positions are kept in flight in a ring of stage
@@ -966,14 +970,16 @@ void gemv_chain_kernel(const ChainArgs a)
         // turn (continuing the turn across tasks); otherwise task t's rows
         // are dealt to all the grid's waves from a rotated start, so that
         // the waves holding one row more than the others differ from task
-        // to task.  Inside a segment the ring is the single-product
-        // kernel's: a position is a row and a stage, advanced with a few
-        // scalar instructions; task switches stay out of that loop.
+        // to task.  The ring is the single-product kernel's, with a position
+        // a task, a row and a stage: it runs on from one segment into the
+        // next (into the wave's next task with rows), so the loads of a
+        // task's first rows are in flight while the wave finishes the
+        // previous task and waits for the new task's x.
         const int wave_id = (int)__builtin_amdgcn_readfirstlane(blockIdx.x * NC + wave);
         const LaneOffs lo = lane_offs<FMT>(lane, a.gshift);
         const int total_waves = gridDim.x * NC;
         // the last wave also moves x: task tlo's here, every later task's
-        // when it enters the task (lead_x)
+        // when it enters the task or passes it (lead_x)
         const bool lead = wave == NC - 1;
         if (lead) {
             // task tlo is entered by every compute wave in the prologue; the
@@ -991,10 +997,9 @@ void gemv_chain_kernel(const ChainArgs a)
         __syncthreads();  // the table, the counters and x of task tlo
         int cur = tlo;  // the last task this wave has counted into
         // Counting into task t (this wave is done with every earlier task).
-        // Before a task that reads earlier outputs, this wave's own stores
-        // complete first (the lead wave then passes them on to the grid): with
-        // the count taken before the task's first weight loads go out, the
-        // wait covers the stores alone.
+        // Before a task that waits for the grid, this wave's own stores
+        // complete first (the lead wave then passes them on to the grid; the
+        // wait also covers the weight loads the ring already has in flight).
         auto arrive = [&](int t) {
             if (DEP && ctl_wait(task(t).ctl)) {
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1048,81 +1053,99 @@ void gemv_chain_kernel(const ChainArgs a)
 
         u32x4 xreg[8];
         float2 acc[1] = {float2{0.0f, 0.0f}};
-        int turn = 0;  // blocked walk: the block's rows before this task, mod NC
-        const int t0 = has_rows ? tlo : nt;
-        for (int t = t0; t <= thi; ++t) {
-            const ChainTask T = task(t);
-            const TaskViews tv = task_views<FMT>(T, a.gshift);
-            int first, step, end;
-            if constexpr (!DEP) {
-                const int start = t == tlo ? rlo : 0;
-                end = (t == tend) ? rend : tv.N;
-                first = start + (wave - turn + NC) % NC;
-                step = NC;
-                turn = (turn + end - start) % NC;
-            } else {
-                first = (int)(((uint32_t)wave_id + (uint32_t)t * 1237u) % (uint32_t)total_waves);
-                step = total_waves;
-                end = tv.N;
+        // The loader: the next position to load, in walk order across the
+        // tasks (task lt, row lrow, stage ls), and the segment of task lt
+        // (rows from its first, lstep apart, below lend); lt > thi once every
+        // position is loaded.  The ring runs on across task boundaries, so a
+        // task's first weights are in flight while the wave finishes the
+        // previous task and waits for the new task's x.
+        int lt = has_rows ? tlo - 1 : thi + 1, lrow = 0, ls = 0, lstep = 1, lend = 0;
+        int turn = 0;  // blocked walk: the block's rows before task lt, mod NC
+        TaskViews ltv = task_views<FMT>(task(0), a.gshift);
+        auto next_task = [&]() {
+            while (++lt <= thi) {
+                const ChainTask T = task(lt);
+                int first;
+                if constexpr (!DEP) {
+                    const int start = lt == tlo ? rlo : 0;
+                    lend = lt == tend ? rend : T.N;
+                    first = start + (wave - turn + NC) % NC;
+                    lstep = NC;
+                    turn = (turn + lend - start) % NC;
+                } else {
+                    first = (int)(((uint32_t)wave_id + (uint32_t)lt * 1237u) % (uint32_t)total_waves);
+                    lstep = total_waves;
+                    lend = T.N;
+                }
+                if (first < lend) {
+                    ltv = task_views<FMT>(T, a.gshift);
+                    lrow = first;
+                    ls = 0;
+                    return;
+                }
             }
+        };
+        // Loads the loader's position into a ring slot (past the walk: an
+        // empty row, whose loads return zeros) and moves the loader on.
+        auto load_next = [&](Stage &st_, ChainPos &p) {
+            const bool live = lt <= thi;
+            p = ChainPos{live ? lt : nt, lrow, ls};
+            load_stage_chain<FMT>(st_, ltv, live ? lrow : ltv.N, live ? ls : 0, lo, a.gshift);
+            if (live && ++ls == ltv.S) {
+                ls = 0;
+                lrow += lstep;
+                if (lrow >= lend)
+                    next_task();
+            }
+        };
+        // The compute side: task ct (views ctv) is the one being computed;
+        // entering task t counts this wave into every task up to t, has the
+        // lead wave copy x of every task up to t, and waits for x of t.
+        int ct = -1, led = tlo;
+        TaskViews ctv = ltv;
+        auto enter = [&](int t) {
             while (cur < t)
                 arrive(++cur);
-            if (first >= end) {
-                if (lead && t > tlo)
-                    lead_x(t);
-                continue;  // no rows here
-            }
-            const int S = tv.S;
-            // positions: rows first, first + step, ...; a row at or past end
-            // loads from an empty view (zeros) and stores nothing
-            auto advance = [&](Pos q) {
-                if (++q.s == S) {
-                    q.s = 0;
-                    q.row += step;
-                }
-                return q;
-            };
-            auto load_pos = [&](Stage &st_, Pos q) {
-                load_stage_chain<FMT>(st_, tv, q.row < end ? q.row : tv.N, q.s, lo, a.gshift);
-            };
-            // the first loads go out before the task's x is awaited (weights
-            // never depend on earlier tasks)
-            Pos pos[P];
-            Stage st[P];
-            pos[0] = Pos{first, 0};
+            if (lead)
+                while (led < t)
+                    lead_x(++led);
+            await_x(t);
+            ctv = task_views<FMT>(task(t), a.gshift);
+            ct = t;
+            if (ctv.S == 1)
+                chain_x_slice(xreg, xb, ctv.xbase, 0, lane);
+        };
+
+        if (has_rows)
+            next_task();
+        ChainPos pos[P];
+        Stage st[P];
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            load_next(st[q], pos[q]);
+        // A round of the ring is never left in the middle (the load waits
+        // stay partial only if every path refills every slot).
+        while (pos[0].t <= thi) {
 #pragma unroll
             for (int q = 0; q < P; ++q) {
-                if (q > 0)
-                    pos[q] = advance(pos[q - 1]);
-                load_pos(st[q], pos[q]);
-            }
-            if (lead && t > tlo)
-                lead_x(t);
-            await_x(t);
-            if (S == 1)
-                chain_x_slice(xreg, xb, tv.xbase, 0, lane);
-            // A round of the ring is never left in the middle (the load
-            // waits stay partial only if every path refills every slot).
-            while (pos[0].row < end) {
-#pragma unroll
-                for (int q = 0; q < P; ++q) {
-                    const Pos cp = pos[q];
-                    // (a position past the segment's last row is not
-                    // computed: its slot is still refilled below)
-                    if (cp.row < end) {
-                        if (S > 1)
-                            chain_x_slice(xreg, xb, tv.xbase, cp.s, lane);
-                        // (x comes from registers: no x view, K or chunk count needed)
-                        compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
-                                                          make_rsrc(nullptr, 0), 0, 0, cp.s, lane,
-                                                          0, laneoff, a.gshift);
-                    }
-                    if (cp.s == S - 1 && cp.row < end) {
+                const ChainPos cp = pos[q];
+                // (a position past the walk is not computed: its slot is
+                // still refilled below)
+                if (cp.t <= thi) {
+                    if (cp.t != ct)
+                        enter(cp.t);
+                    if (ctv.S > 1)
+                        chain_x_slice(xreg, xb, ctv.xbase, cp.s, lane);
+                    // (x comes from registers: no x view, K or chunk count needed)
+                    compute_stage<FMT, ACT, 1, X_REG>(st[q], acc, tbl, nullptr, xreg,
+                                                      make_rsrc(nullptr, 0), 0, 0, cp.s, lane, 0,
+                                                      laneoff, a.gshift);
+                    if (cp.s == ctv.S - 1) {
                         const float out = row_sum(acc[0]);
                         acc[0] = float2{0.0f, 0.0f};
                         // through a global (not flat) pointer: a flat store
                         // may write LDS, so LDS reads after it would wait
-                        auto *const yp = (__attribute__((address_space(1))) uint16_t *)(tv.y + cp.row);
+                        auto *const yp = (__attribute__((address_space(1))) uint16_t *)(ctv.y + cp.row);
                         const uint16_t yb = (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(out) : f2h_bits(out));
                         if (lane == 0) {
                             if constexpr (DEP)  // later tasks may read it (coherent store)
@@ -1131,14 +1154,17 @@ void gemv_chain_kernel(const ChainArgs a)
                                 *yp = yb;
                         }
                     }
-                    pos[q] = advance(pos[(q + P - 1) % P]);
-                    load_pos(st[q], pos[q]);
                 }
+                load_next(st[q], pos[q]);
             }
         }
-        // waves with no rows in the last tasks still count into them
+        // the tasks after this wave's last position: still counted into,
+        // and (lead wave) their x copied for the other waves
         while (cur < thi)
             arrive(++cur);
+        if (lead)
+            while (led < thi)
+                lead_x(++led);
     }
     wait_vm<0>();  // no LDS DMA may be in flight when the workgroup ends
     __syncthreads();
