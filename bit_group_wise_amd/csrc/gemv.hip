@@ -647,8 +647,9 @@ void gemv_kernel(const uint16_t *__restrict__ x, int M, const uint8_t *__restric
 // task t is copied in (by DMA) once every compute wave has entered the task
 // after the last one that used those slots (the gate, computed on the host)
 // and then published; a compute wave entering task t waits only for that.
-// All 16 waves of a workgroup compute; the last one also moves x, when it
-// enters a task, after its own weight loads for the task are out.  (A
+// All 16 waves of a workgroup compute; the last one also moves x, for each
+// task in turn once it has no earlier positions left to compute, with its
+// own weight loads for the task already out.  (A
 // separate loader wave, which copied x as early as the gates allowed, left
 // its SIMD a wave short of the others: 16 compute waves measured 1 % faster
 // on the independent decode token and 8 % on the dependent one.)
