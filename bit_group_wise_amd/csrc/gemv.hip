@@ -216,9 +216,9 @@ struct Stage {
     u32x4 cw[2];
     float sc[2];
     float zf[2];
-    // double quantization: the constants of the (at most 3) runs of kDqRun
-    // groups the row touches (scalar registers) and the row's first group's
-    // position in the first of them
+    // double quantization: the constants of the runs of kDqRun groups the
+    // stage touches (at most 2, and the next; scalar registers) and the
+    // stage's first group's position in the first of them
     float s2[3];
     int zpar;
 };
@@ -297,17 +297,21 @@ __device__ __forceinline__ void load_stage(Stage &st, const RowRef &r, int s, co
         }
     }
     if constexpr (FMT == Q4_NF4_DQ) {
-        // One scalar load of the constants of the row's runs (a row of at
-        // most 16384 / 32 groups touches at most 3 runs; the last ones may
-        // read the buffer's padding, never used for a real group), rather
-        // than a vector load per stage.  The group's run is picked when the
-        // stage is computed.
+        // One scalar load of the constants of the runs the stage touches,
+        // from the run holding its first group (a stage of 4096 weights
+        // holds at most 128 groups, so it touches at most 2 runs, whatever
+        // the row's length; the last constants loaded may be the buffer's
+        // padding, never used for a real group), rather than a vector load
+        // per stage.  The group's run is picked when the stage is computed.
+        // A row past the end reads the first constants (its codes are 0).
+        const int u0 = r.zpar + gs;  // the stage's first group, from the start of the row's first run
         typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
-        const f32x4a4 c = *(const __attribute__((address_space(4))) f32x4a4 *)r.s2;
+        const f32x4a4 c =
+            *(const __attribute__((address_space(4))) f32x4a4 *)(r.s2 + (r.live ? u0 / kDqRun : 0));
         st.s2[0] = c[0];
         st.s2[1] = c[1];
         st.s2[2] = c[2];
-        st.zpar = r.zpar;
+        st.zpar = u0 & (kDqRun - 1);
     }
 }
 
@@ -396,9 +400,10 @@ __device__ __forceinline__ void compute_stage(const Stage &st, float2 (&acc)[MT]
             // two runs: the run of its first group (ra) and the next
             // (rb), picked per half from wave-uniform values; a lane
             // takes rb when its group is at or past the run boundary.
-            // Groups are counted from the start of the row's first run.
-            const int u = st.zpar + ((kStageChunks * 32 * s + 64 * 32 * h) >> gshift);
-            const int r0 = u >> 8;                         // 0..2
+            // Groups are counted from the start of the run holding the
+            // stage's first group.
+            const int u = st.zpar + ((64 * 32 * h) >> gshift);
+            const int r0 = u >> 8;                         // 0..1
             const int thr = 256 * (r0 + 1) - u;            // first lane group in rb
             const uint32_t a0 = std::bit_cast<uint32_t>(st.s2[0]);
             const uint32_t a1 = std::bit_cast<uint32_t>(st.s2[1]);

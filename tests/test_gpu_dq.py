@@ -97,3 +97,25 @@ def test_dq_chain_matches_gemv():
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(zip(outs, ref)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"task {i} differs"
+
+
+def test_dq_long_rows_gemv():
+    """Rows longer than the runs of 256 groups a stage can touch (K / g of
+    769, 641 and 528 groups, so runs also start inside rows), with the
+    magnitude changing every 2048 columns so that every run has its own
+    second-level constant: the M <= 2 GEMV (which picks a stage's runs from
+    the stage's first group) and the skinny product against the oracle."""
+    for g, K in [(32, 24608), (64, 41024), (128, 67584)]:
+        N = 5
+        v = synth.normal_f32((N, K), 4100 + g, 0.02, 0.0)
+        v *= np.exp2((np.arange(K) // 2048) % 9 - 4).astype(np.float32)[None, :]
+        w = synth.to_f16_bits(v)
+        q, (oc, os_, oz) = assert_quant_equal(q4.NF4_DQ, g, w, tag=f"dq long rows g{g}")
+        for act in (q4.BF16, q4.F16):
+            for M in (1, 2, 4):
+                print(f"dq long rows g{g} K{K} act{act} M{M}", flush=True)
+                xb = synth.act_bits(M, K, 4200 + M, act)
+                y = q4.gemv(dev16(xb, act), q)
+                torch.cuda.synchronize()
+                yr, ad = oracle.matmul(q4.NF4_DQ, g, act, xb, oc, os_, oz, N, K)
+                assert_product_ok(y, yr, ad, tag=f"dq long rows g{g} act{act} M{M}")
