@@ -1,7 +1,9 @@
-"""The largest K q4_gemm accepts (Q4_GEMM_MAX_K): a 256-row tile of x then
-spans exactly 2^31 bytes, the end of the GEMM's 32-bit buffer view.  The
-sampled x rows are zero except near both ends of K, so a dword the view
-failed to cover (read as zero) would change those outputs completely."""
+"""Long rows.  The largest K q4_gemm accepts (Q4_GEMM_MAX_K): a 256-row tile
+of x then spans exactly 2^31 bytes, the end of the GEMM's 32-bit buffer
+view.  The sampled x rows are zero except near both ends of K, so a dword
+the view failed to cover (read as zero) would change those outputs
+completely.  And q4_gemv on rows of about half a million weights, every
+format."""
 
 import numpy as np
 import pytest
@@ -47,3 +49,26 @@ def test_gemm_at_max_k():
     assert_product_ok(y[[M - 1]], yr, ad, tag="gemm K = Q4_GEMM_MAX_K, last dword")
     del x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", [q4.NF4, q4.INT4_SYM, q4.INT4_ASYM, q4.NF4_DQ, q4.FP4])
+def test_gemv_long_rows(fmt):
+    """q4_gemv on rows of 524,416 weights (129 stages of the M <= 2 GEMV, x
+    read from L2 instead of staged in LDS; for double quantization, 16 to 65
+    runs of 256 groups per row), the magnitude changing every 4096 columns,
+    at M = 1, 2 (vector ALUs) and 4, 16 (skinny product) against the
+    oracle."""
+    K, N = 524416, 9
+    for g in (32, 128):
+        v = synth.normal_f32((N, K), 950 + g, 0.02)
+        v *= np.exp2((np.arange(K) // 4096) % 9 - 4).astype(np.float32)[None, :]
+        w = synth.to_f16_bits(v)
+        oc, os_, oz = oracle.quantize(fmt, g, w)
+        q = q4.quantize(dev16(w), fmt, g)
+        for M in (1, 2, 4, 16):
+            print(f"gemv long rows fmt{fmt} g{g} M{M}", flush=True)
+            xb = synth.act_bits(M, K, 960 + M, q4.BF16)
+            y = q4.gemv(dev16(xb, q4.BF16), q)
+            torch.cuda.synchronize()
+            yr, ad = oracle.matmul(fmt, g, q4.BF16, xb, oc, os_, oz, N, K)
+            assert_product_ok(y, yr, ad, tag=f"gemv long rows fmt{fmt} g{g} M{M}")
