@@ -185,6 +185,7 @@ def main():
     qw_dq = [[q4.quantize(w, q4.NF4_DQ, 64) for w in mats] for mats in fp16]
     torch.cuda.synchronize()
     w_bytes_dq = sum(q.nbytes() for row in qw_dq for q in row)
+    log("quantized all weights (NF4, then NF4 with double-quantized absmax)")
     del fp16
     torch.cuda.empty_cache()
 
@@ -258,6 +259,7 @@ def main():
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms = e0.elapsed_time(e1) / args.steps
     value = w_bytes / (ms * 1e-3) / 1e9
+    log(f"decode token timed: {ms:.4f} ms per step, {value:.1f} GB/s")
 
     timed = _timer(torch, stream)
     reps = max(args.steps // 5, 3)
@@ -290,6 +292,7 @@ def main():
         raise RuntimeError("double-quantized chain differs from single-product launches")
     del ref_dq
     dq_ms = timed(lambda: run_chains(chains_dq), max(args.steps // 2, 3))
+    log("dependent chain, single launches and double-quantized token timed")
     launch_ms = [evs[i].elapsed_time(evs[i + 1]) for evs in lev for i in range(len(indep))]
     chain_avg_us = sum(launch_ms) / len(launch_ms) * 1e3
     bytes_per_chain = w_bytes / n_chain
@@ -298,6 +301,7 @@ def main():
     extra = {}
     if not args.skip_extra:
         extra = extra_legs(torch, q4, dev, stream)
+        log("matrix-core, codec and single-matrix legs timed")
         extra["gemv_configs_cold"] = config_gemvs(torch, q4, dev, stream)
         extra["codec_configs_cold"] = codec_configs(torch, q4, dev, stream)
         extra["hbm_copy_ceiling"] = copy_ceiling(torch, dev, stream)
