@@ -27,7 +27,8 @@ launch stream:
     product dX = dY . What on the same weight, after 400 warm-up calls each,
   * the unfused path (dequantize to bf16, then torch.matmul / hipBLASLt) at
     the prefill shape and at M = 16 on an 11008x4096 NF4 weight, beside the
-    fused kernels,
+    fused kernels, and both on the prefill weight at M = 64 ... 1024 (where
+    the fused product stops beating the unfused path),
   * single-matrix GEMVs on cold weights (rotating copies over 512 MiB):
     NF4 g64 1024x1024 and INT4-sym g128 4096x4096 at M = 1, NF4 g64
     11008x4096 and 4096x11008 at M = 1, 4, 16,
@@ -642,6 +643,20 @@ def extra_legs(torch, q4, dev, stream):
         torch.matmul(x16, o16.t(), out=y16)
     u16 = timed(unfused16, 20)
     f16t = timed(lambda: q4.gemv(x16, q16, out=y16), 20)
+    # where the fused product stops beating the unfused path: the same
+    # weight at prefill widths between the two
+    sweep = {}
+    for m in (64, 128, 256, 512, 1024):
+        xm, ym, ybm = x[:m], y[:m], yb[:m]
+
+        def unfused_m():
+            q4.dequantize(q, torch.bfloat16, out=out)
+            torch.matmul(xm, out.t(), out=ybm)
+        fm = timed(lambda: q4.gemm(xm, q, out=ym), 20, warm=100)
+        um = timed(unfused_m, 20, warm=100)
+        sweep[f"M{m}"] = {"fused_ms": round(fm, 4), "unfused_ms": round(um, 4),
+                          "fused_TFLOPs": round(2.0 * m * N * K / (fm * 1e-3) / 1e12, 1),
+                          "fused_over_unfused": round(um / fm, 3)}
     # the backward product through the same frozen weight (QLoRA's dX):
     # dY [2048, 14336] . What -> [2048, 4096], and the unfused equivalent
     gen = torch.Generator(device=dev)
@@ -670,7 +685,8 @@ def extra_legs(torch, q4, dev, stream):
             "fused_over_unfused_prefill": round(ut / gt, 3),
             "decode_M16_nf4_11008x4096_unfused_ms": round(u16, 4),
             "decode_M16_nf4_11008x4096_fused_ms": round(f16t, 4),
-            "fused_over_unfused_M16": round(u16 / f16t, 3)},
+            "fused_over_unfused_M16": round(u16 / f16t, 3),
+            "prefill_m_sweep_int4asym_g32_14336x4096": sweep},
         "dequantize_14336x4096_asym_bf16": {"ms": round(dt, 4),
                                              "GBps": round(codec_bytes / (dt * 1e-3) / 1e9, 1)},
         "quantize_14336x4096_asym": {"ms": round(qt, 4),

@@ -1,5 +1,5 @@
-// gemv_mfma.hip -- skinny product y[M, N] = x[M, K] . What^T for M <= 16 on
-// the matrix cores.
+// gemv_mfma.hip -- skinny product y[M, N] = x[M, K] . What^T for small M on
+// the matrix cores (q4_gemv with 3 <= M <= 16, q4_gemm with M <= 96).
 //
 // Method ("Loading a model in 4-bit", "Where the accuracy goes"; "INT4
 // Quantization > Practical Implementation with bitsandbytes"): the weights
@@ -12,7 +12,9 @@
 //
 // gfx950 mapping:
 //  * A workgroup owns RB blocks of 16 weight rows (one MFMA operand each)
-//    and all M <= 16 activation rows; its 8 waves split K into steps of
+//    and MT blocks of 16 activation rows (MT = 1, 2 or 4: up to 64 rows per
+//    launch; each dequantized weight fragment feeds MT products); more rows
+//    run as consecutive launches over row slices.  Its 8 waves split K into steps of
 //    128, interleaved (wave w takes steps w, w + 8, ...).  A step's x
 //    fragment serves all RB blocks, so each workgroup reads x once for RB
 //    blocks; RB (1, 2 or 4) is the largest that still gives every compute
@@ -27,8 +29,9 @@
 //    Every load is contiguous; x rows past M and k past K are sent out of
 //    range and read zeros.
 //  * A 2-deep ring of steps keeps the next step's loads in flight.
-//  * The 8 partial 16 x 16 tiles meet in LDS and are summed in wave order
-//    (a fixed order, so the result does not depend on timing).
+//  * The 8 partial 16 x 16 tiles of each (row block, activation block) meet
+//    in LDS and are summed in wave order (a fixed order, so the result does
+//    not depend on timing).
 //  * Double-quantized NF4 absmax: the lane loads its group's 8-bit code and
 //    its run's binary32 constant and recovers the absmax with one product.
 #include "q4_common.hpp"
@@ -41,6 +44,7 @@ namespace {
 constexpr int kSkWaves = 8;
 constexpr int kSkBlock = 64 * kSkWaves;
 constexpr int kSkStep = 128;  // k per step
+constexpr int kSkMaxRows = 64;  // activation rows per launch (4 blocks of 16)
 #ifndef Q4_SK_RING
 #define Q4_SK_RING 2
 #endif
@@ -56,16 +60,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void *base, int6
 // One step's operands for a lane: for each of the RB row blocks, 32 codes
 // and their group's scale (and asym zero-point, or NF4_DQ run constant);
 // and 32 activations of one x row, shared by the blocks.
-template <int FMT, int RB>
+template <int FMT, int RB, int MT>
 struct SkStep {
     u32x4 cw[RB];
     uint32_t sraw[RB];
     uint32_t zraw[RB];
     int zsh[RB];
-    u32x4 xv[4];
+    u32x4 xv[MT][4];
 };
 
-template <int FMT, int ACT, int RB>
+template <int FMT, int ACT, int RB, int MT>
 __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int N, int K, int gshift,
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
 {
     constexpr int LF = level_fmt(FMT);
     __shared__ float2 ptbl[LF == Q4_NF4 ? 256 : 1];
-    __shared__ f32x4 part[kSkWaves][RB][64];
+    __shared__ f32x4 part[kSkWaves][RB][MT][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
     const __amdgpu_buffer_rsrc_t xr = sk_rsrc(x, (int64_t)M * K * 2);
 
     const int nsteps = (K + kSkStep - 1) / kSkStep;
-    auto load = [&](SkStep<FMT, RB> &st, int step) {
+    auto load = [&](SkStep<FMT, RB, MT> &st, int step) {
         const int k = step * kSkStep + 32 * q;  // the lane's first k
         const bool in = step < nsteps && k < K;
 #pragma unroll
@@ -137,28 +141,34 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
                 st.zraw[b] = 0;
             }
         }
-        const bool xin = in && r < M;
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-            st.xv[d] = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, xin ? 2 * (r * K + k + 8 * d) : -16, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + r;  // the lane's activation row
+            const bool xin = in && m < M;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                st.xv[mt][d] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, xin ? 2 * (m * K + k + 8 * d) : -16, 0, 0);
+        }
     };
 
     // the wave's steps: wave, wave + 8, ...
-    SkStep<FMT, RB> ring[kSkRing];
+    SkStep<FMT, RB, MT> ring[kSkRing];
 #pragma unroll
     for (int i = 0; i < kSkRing; ++i)
         load(ring[i], wave + kSkWaves * i);
     __syncthreads();  // the level-pair table
 
-    f32x4 acc[RB];
+    f32x4 acc[RB][MT];
 #pragma unroll
     for (int b = 0; b < RB; ++b)
-        acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[b][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int step = wave; step < nsteps; step += kSkWaves * kSkRing) {
 #pragma unroll
         for (int i = 0; i < kSkRing; ++i) {
-            SkStep<FMT, RB> &st = ring[i];
+            SkStep<FMT, RB, MT> &st = ring[i];
             // a step past the end is not computed (its slot is still
             // refilled below, so the load waits stay partial)
 #pragma unroll
@@ -186,55 +196,73 @@ __global__ __launch_bounds__(kSkBlock) void gemv_mfma_kernel(
                             lp[e] = ptbl[(st.cw[b][d] >> (8 * e)) & 0xffu];
                     }
                     const u32x4 wf = dequant8<FMT, ACT>(st.cw[b][d], s, bias, lp);
-                    acc[b] = mfma<ACT>(wf, st.xv[d], acc[b]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[b][mt] = mfma<ACT>(wf, st.xv[mt][d], acc[b][mt]);
                 }
             }
             load(st, step + kSkWaves * (i + kSkRing));
         }
     }
 
-    // sum the 8 partial tiles of each block in wave order; lane l holds rows
-    // 4 q + v of the block against activation row r
+    // sum the 8 partial tiles of each (row block, activation block) in wave
+    // order; lane l holds rows 4 q + v of the row block against activation
+    // row 16 mt + r
 #pragma unroll
     for (int b = 0; b < RB; ++b)
-        part[wave][b][lane] = acc[b];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            part[wave][b][mt][lane] = acc[b][mt];
     __syncthreads();
-    if (wave < RB) {
-        const int b = wave;
-        f32x4 t = part[0][b][lane];
+    for (int t = wave; t < RB * MT; t += kSkWaves) {
+        const int b = t / MT, mt = t % MT;
+        f32x4 u0 = part[0][b][mt][lane];
 #pragma unroll
         for (int w = 1; w < kSkWaves; ++w) {
-            const f32x4 u = part[w][b][lane];
-            t = f32x4{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
+            const f32x4 u = part[w][b][mt][lane];
+            u0 = f32x4{u0[0] + u[0], u0[1] + u[1], u0[2] + u[2], u0[3] + u[3]};
         }
-        const int m = r;
+        const int m = 16 * mt + r;
         const int n = n0 + 16 * b + 4 * q;
         if (m < M) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if (n + v < N)
                     y[(int64_t)m * N + n + v] =
-                        (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(t[v]) : f2h_bits(t[v]));
+                        (uint16_t)(ACT == Q4_BF16 ? f2bf_bits(u0[v]) : f2h_bits(u0[v]));
             }
         }
     }
 }
 
-template <int FMT, int RB>
-hipError_t launch_sk_rb(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
+template <int FMT, int RB, int MT>
+hipError_t launch_sk_mt(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
                         const void *scales, const uint8_t *zeros, int64_t N, int64_t K, int gshift,
                         void *y, hipStream_t s)
 {
     const unsigned blocks = (unsigned)((N + 16 * RB - 1) / (16 * RB));
     if (act_t == Q4_BF16)
-        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_BF16, RB>), dim3(blocks), dim3(kSkBlock), 0, s,
-                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
-                           (uint16_t *)y);
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_BF16, RB, MT>), dim3(blocks), dim3(kSkBlock),
+                           0, s, (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K,
+                           gshift, (uint16_t *)y);
     else
-        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_F16, RB>), dim3(blocks), dim3(kSkBlock), 0, s,
-                           (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K, gshift,
-                           (uint16_t *)y);
+        hipLaunchKernelGGL((gemv_mfma_kernel<FMT, Q4_F16, RB, MT>), dim3(blocks), dim3(kSkBlock),
+                           0, s, (const uint16_t *)x, M, codes, scales, zeros, (int)N, (int)K,
+                           gshift, (uint16_t *)y);
     return hipGetLastError();
+}
+
+// Activation blocks of 16 rows per launch: 1, 2 or 4 (M <= 16, 32, 64).
+template <int FMT, int RB>
+hipError_t launch_sk_rb(q4_dtype act_t, const void *x, int M, const uint8_t *codes,
+                        const void *scales, const uint8_t *zeros, int64_t N, int64_t K, int gshift,
+                        void *y, hipStream_t s)
+{
+    if (M <= 16)
+        return launch_sk_mt<FMT, RB, 1>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
+    if (M <= 32)
+        return launch_sk_mt<FMT, RB, 2>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
+    return launch_sk_mt<FMT, RB, 4>(act_t, x, M, codes, scales, zeros, N, K, gshift, y, s);
 }
 
 // Row blocks per workgroup: the blocks spread over the compute units
@@ -266,18 +294,34 @@ hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, i
                             int64_t N, int64_t K, void *y, hipStream_t s)
 {
     const int gshift = g == 32 ? 5 : (g == 64 ? 6 : 7);
-    switch (f) {
-    case Q4_NF4:
-        return launch_sk_fmt<Q4_NF4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
-    case Q4_FP4:
-        return launch_sk_fmt<Q4_FP4>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
-    case Q4_NF4_DQ:
-        return launch_sk_fmt<Q4_NF4_DQ>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
-    case Q4_INT4_SYM:
-        return launch_sk_fmt<Q4_INT4_SYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
-    default:
-        return launch_sk_fmt<Q4_INT4_ASYM>(act_t, x, (int)M, codes, scales, zeros, N, K, gshift, y, s);
+    // up to kSkMaxRows activation rows per launch; more run as consecutive
+    // launches over row slices of x and y (each reads every weight once)
+    for (int64_t m0 = 0; m0 < M; m0 += kSkMaxRows) {
+        const int mc = (int)(M - m0 < kSkMaxRows ? M - m0 : kSkMaxRows);
+        const void *xc = (const uint16_t *)x + m0 * K;
+        void *yc = (uint16_t *)y + m0 * N;
+        hipError_t e;
+        switch (f) {
+        case Q4_NF4:
+            e = launch_sk_fmt<Q4_NF4>(act_t, xc, mc, codes, scales, zeros, N, K, gshift, yc, s);
+            break;
+        case Q4_FP4:
+            e = launch_sk_fmt<Q4_FP4>(act_t, xc, mc, codes, scales, zeros, N, K, gshift, yc, s);
+            break;
+        case Q4_NF4_DQ:
+            e = launch_sk_fmt<Q4_NF4_DQ>(act_t, xc, mc, codes, scales, zeros, N, K, gshift, yc, s);
+            break;
+        case Q4_INT4_SYM:
+            e = launch_sk_fmt<Q4_INT4_SYM>(act_t, xc, mc, codes, scales, zeros, N, K, gshift, yc, s);
+            break;
+        default:
+            e = launch_sk_fmt<Q4_INT4_ASYM>(act_t, xc, mc, codes, scales, zeros, N, K, gshift, yc, s);
+            break;
+        }
+        if (e != hipSuccess)
+            return e;
     }
+    return hipSuccess;
 }
 
 }  // namespace q4

@@ -11,6 +11,10 @@
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 
+#ifndef Q4_GEMM_SKINNY_MAX_M
+#define Q4_GEMM_SKINNY_MAX_M 96
+#endif
+
 // The sync words of q4_gemv_chain_static: one chain's finished-workgroup
 // count, timeout flag and grid-barrier words (Q4_GEMV_CHAIN_SYNC_BYTES),
 // in static device memory that each GPU holds for the life of the process.
@@ -196,9 +200,9 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
         return st;
     if (K > Q4_GEMM_MAX_K)
         return Q4_EUNSUPPORTED;
-    // up to 16 activation rows: the skinny product (a 256-row tile would be
-    // mostly empty)
-    if (M <= 16)
+    // up to Q4_GEMM_SKINNY_MAX_M activation rows: the skinny product, 64
+    // rows per launch (256-row tiles would leave most units idle)
+    if (M <= Q4_GEMM_SKINNY_MAX_M)
         return from_hip(q4::launch_gemv_mfma(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                              (hipStream_t)stream));
     return from_hip(q4::launch_gemm(f, g, act_t, x, M, codes, scales, zeros, N, K, y,

@@ -41,7 +41,8 @@ hipError_t launch_dequantize(q4_format f, int g, const uint8_t *codes, const voi
 hipError_t launch_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                        const uint8_t *codes, const void *scales, const uint8_t *zeros,
                        int64_t N, int64_t K, void *y, hipStream_t s);
-// Skinny product (M <= 16) on the matrix cores.
+// Skinny product on the matrix cores: up to 64 activation rows per launch,
+// more as consecutive launches over row slices.
 hipError_t launch_gemv_mfma(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                             const uint8_t *codes, const void *scales, const uint8_t *zeros,
                             int64_t N, int64_t K, void *y, hipStream_t s);

@@ -170,7 +170,10 @@ q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
  * tiles are dequantized to the activation dtype on the fly (each value as
  * q4_dequantize writes it) and multiplied on the matrix cores with fp32
  * accumulation; y is rounded once to act_t ("Where the accuracy goes").
- * M <= 16 runs as the skinny product q4_gemv uses for 3 <= M <= 16.
+ * M <= 96 runs as the skinny product q4_gemv uses for 3 <= M <= 16, with
+ * one, two or four blocks of 16 activation rows per launch (up to 64 rows)
+ * and, past 64 rows, consecutive launches over row slices of x and y, all on
+ * the caller's stream; larger M runs in 256 x 256 tiles.
  * K > Q4_GEMM_MAX_K returns Q4_EUNSUPPORTED. */
 #define Q4_GEMM_MAX_K 4194304
 q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,

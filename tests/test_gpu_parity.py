@@ -189,6 +189,22 @@ def test_gemm_tolerance(fmt, act, M, N, K, g):
     assert_product_ok(y, yr, ad, tag=f"gemm fmt{fmt} act{act} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("act", [q4.F16, q4.BF16])
+def test_gemm_skinny_row_blocks_and_slices(fmt, act):
+    """q4_gemm up to 96 activation rows runs the skinny product with 1, 2 or
+    4 blocks of 16 rows per launch, and past 64 rows as consecutive launches
+    over row slices: every row count class, ragged N and K, against the
+    oracle."""
+    for M, N, K, g in [(31, 200, 288, 32), (33, 136, 1088, 64), (64, 72, 384, 128),
+                       (65, 200, 288, 32), (80, 136, 576, 64), (96, 1000, 160, 32)]:
+        q, (oc, os_, oz), xb = _setup(fmt, g, N, K, M, act, seed=M + N + K)
+        y = q4.gemm(dev16(xb, act), q)
+        torch.cuda.synchronize()
+        yr, ad = oracle.matmul(fmt, g, act, xb, oc, os_, oz, N, K)
+        assert_product_ok(y, yr, ad, tag=f"gemm fmt{fmt} act{act} {M}x{N}x{K}")
+
+
 def test_gemm_matches_library_matmul():
     """Cross-check against torch.matmul on the dequantized weights."""
     fmt, g, act, M, N, K = q4.INT4_ASYM, 32, q4.BF16, 256, 384, 1024
