@@ -50,9 +50,15 @@ namespace q4 {
 namespace {
 
 constexpr int BM = 256;                       // x rows per tile
-constexpr int BN = 256;                       // W rows per tile
+#ifndef Q4_GEMM_BN
+#define Q4_GEMM_BN 256
+#endif
+#ifndef Q4_GEMM_WAVES
+#define Q4_GEMM_WAVES 8
+#endif
+constexpr int BN = Q4_GEMM_BN;                // W rows per tile
 constexpr int BK = 64;                        // k per step
-constexpr int kWaves = 8;                     // waves per workgroup
+constexpr int kWaves = Q4_GEMM_WAVES;         // waves per workgroup (BN / 32)
 constexpr int kBlock = 64 * kWaves;
 constexpr int ROW_BYTES = BK * 2;             // one staged x row
 constexpr int X_BYTES = BM * ROW_BYTES;

@@ -11,6 +11,9 @@
 #include "q4_common.hpp"
 #include "q4_internal.hpp"
 
+#ifndef Q4_GEMM_BN128_MAX_M
+#define Q4_GEMM_BN128_MAX_M 512
+#endif
 #ifndef Q4_GEMM_SKINNY_MAX_M
 #define Q4_GEMM_SKINNY_MAX_M 96
 #endif
@@ -205,6 +208,11 @@ q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
     if (M <= Q4_GEMM_SKINNY_MAX_M)
         return from_hip(q4::launch_gemv_mfma(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                              (hipStream_t)stream));
+    // up to Q4_GEMM_BN128_MAX_M rows: tiles of 128 weight rows (twice the
+    // workgroups of the 256-row tiles, which leave units idle below M = 1024)
+    if (M <= Q4_GEMM_BN128_MAX_M)
+        return from_hip(q4::launch_gemm_bn128(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
+                                              (hipStream_t)stream));
     return from_hip(q4::launch_gemm(f, g, act_t, x, M, codes, scales, zeros, N, K, y,
                                     (hipStream_t)stream));
 }

@@ -57,5 +57,9 @@ hipError_t launch_gemm_dx(q4_format f, int g, q4_dtype act_t, const void *dy, in
 hipError_t launch_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
                        const uint8_t *codes, const void *scales, const uint8_t *zeros,
                        int64_t N, int64_t K, void *y, hipStream_t s);
+// The same with 128-row weight tiles (4 waves per workgroup), for middle M.
+hipError_t launch_gemm_bn128(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
+                       const uint8_t *codes, const void *scales, const uint8_t *zeros,
+                       int64_t N, int64_t K, void *y, hipStream_t s);
 
 }  // namespace q4

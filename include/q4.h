@@ -173,7 +173,8 @@ q4_status q4_gemv(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
  * M <= 96 runs as the skinny product q4_gemv uses for 3 <= M <= 16, with
  * one, two or four blocks of 16 activation rows per launch (up to 64 rows)
  * and, past 64 rows, consecutive launches over row slices of x and y, all on
- * the caller's stream; larger M runs in 256 x 256 tiles.
+ * the caller's stream; 97 <= M <= 512 runs in tiles of 256 activation rows
+ * by 128 weight rows, larger M in 256 x 256 tiles (the same bits either way).
  * K > Q4_GEMM_MAX_K returns Q4_EUNSUPPORTED. */
 #define Q4_GEMM_MAX_K 4194304
 q4_status q4_gemm(q4_format f, int g, q4_dtype act_t, const void *x, int64_t M,
